@@ -1,0 +1,203 @@
+"""Causal attention forward (prefill) for AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over ``libattn_fwd_causal.so`` (C ABI: ``include/attn_fwd_causal.h``).
+Every step of the computation runs in the library's HIP kernels; this module only
+checks tensor metadata and passes device pointers, sizes and the current HIP stream.
+PyTorch serves as the device allocator and stream provider.
+
+Functions mirror the C entry points:
+    attn_fwd_causal_fp8(q, k, v, q_descale, k_descale, v_descale, softmax_scale=None)
+    attn_fwd_causal_bf16(q, k, v, softmax_scale=None)
+    attn_fwd_causal_mla(q, k, v, q_descale, k_descale, v_descale, softmax_scale=None)
+    quantize_e4m3(x) -> (codes, descale)      round_bf16(x) -> bf16 tensor
+Tensors are BSHD: q, k [B, S, H, d_qk], v [B, S, H, d_v]; outputs out [B, S, H, d_v]
+(bfloat16) and lse [B, H, S] (float32).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn_fwd_causal.so")
+
+_STATUS = {0: "ok", -1: "null pointer", -2: "unsupported shape", -3: "misaligned pointer",
+           -4: "tensor too large", -5: "invalid argument", -6: "kernel launch failed", -7: "no usable HIP device"}
+
+
+class AttnError(RuntimeError):
+    def __init__(self, fn, code):
+        super().__init__(f"{fn}: {code} ({_STATUS.get(code, 'unknown')})")
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """Load the HIP library; raises if it has not been built (no fallback path exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with python -m bf16_causal_flashattention_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        P, F, I, I64 = ctypes.c_void_p, ctypes.c_float, ctypes.c_int, ctypes.c_int64
+        L.attn_fwd_causal_fp8.argtypes = [P, P, P, P, P, F, F, F, F, I, I, I, I, I, P]
+        L.attn_fwd_causal_mla.argtypes = [P, P, P, P, P, F, F, F, F, I, I, I, I, I, P]
+        L.attn_fwd_causal_fp8_debug.argtypes = [P, P, P, P, P, F, F, F, F, I, I, I, I, I, P, P, P]
+        L.attn_fwd_causal_bf16.argtypes = [P, P, P, P, P, F, I, I, I, I, I, P]
+        L.attn_quantize_e4m3.argtypes = [P, I64, P, P, P, P]
+        L.attn_round_bf16.argtypes = [P, I64, P, P]
+        L.attn_default_grid.argtypes = [I, I, I, I]
+        L.attn_schedule.argtypes = [I, I, I, I, P, I64]
+        L.attn_schedule.restype = I64
+        L.attn_status_string.argtypes = [I]
+        L.attn_status_string.restype = ctypes.c_char_p
+        for name in ("attn_fwd_causal_fp8", "attn_fwd_causal_mla", "attn_fwd_causal_fp8_debug",
+                     "attn_fwd_causal_bf16", "attn_quantize_e4m3", "attn_round_bf16", "attn_default_grid"):
+            getattr(L, name).restype = I
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(fn, rc):
+    if rc != 0:
+        raise AttnError(fn, rc)
+
+
+def _fp8_view(t):
+    if t.dtype == torch.float8_e4m3fn:
+        return t
+    if t.dtype == torch.uint8:
+        return t.view(torch.float8_e4m3fn)
+    raise TypeError(f"expected float8_e4m3fn (OCP e4m3, not fnuz) or uint8 codes, got {t.dtype}")
+
+
+def _outputs(q, v, out, lse):
+    B, S, H, _ = q.shape
+    dv = v.shape[3]
+    if out is None:
+        out = torch.empty((B, S, H, dv), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    return out, lse
+
+
+def _meta(q, k, v, out, lse):
+    for t in (q, k, v, out, lse):
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous and on the GPU")
+    if out.dtype != torch.bfloat16 or lse.dtype != torch.float32:
+        raise TypeError("out must be bfloat16 and lse float32")
+    B, S, H, dqk = q.shape
+    if tuple(k.shape) != (B, S, H, dqk) or tuple(v.shape[:3]) != (B, S, H):
+        raise ValueError("q, k, v shapes disagree")
+    dv = v.shape[3]
+    if tuple(out.shape) != (B, S, H, dv) or tuple(lse.shape) != (B, H, S):
+        raise ValueError("out / lse shapes disagree")
+    return B, S, H, dqk, dv
+
+
+def _fp8_call(fn_name, q, k, v, q_descale, k_descale, v_descale, softmax_scale, out, lse, debug=None):
+    q, k, v = _fp8_view(q), _fp8_view(k), _fp8_view(v)
+    out, lse = _outputs(q, v, out, lse)
+    B, S, H, dqk, dv = _meta(q, k, v, out, lse)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(dqk)
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), float(q_descale), float(k_descale),
+            float(v_descale), float(softmax_scale), B, H, S, dqk, dv]
+    if debug is not None:
+        args += [_ptr(debug[0]), _ptr(debug[1])]
+    _check(fn_name, getattr(lib(), fn_name)(*args, _stream()))
+    return out, lse
+
+
+def attn_fwd_causal_fp8(q, k, v, q_descale, k_descale, v_descale, softmax_scale=None, out=None, lse=None):
+    """FP8 e4m3 causal attention, d_qk = d_v = 128, lean P.  Returns (out bf16, lse fp32)."""
+    return _fp8_call("attn_fwd_causal_fp8", q, k, v, q_descale, k_descale, v_descale, softmax_scale, out, lse)
+
+
+def attn_fwd_causal_mla(q, k, v, q_descale, k_descale, v_descale, softmax_scale=None, out=None, lse=None):
+    """FP8 e4m3 causal attention at the MLA shape d_qk = 192, d_v = 128, exact P."""
+    return _fp8_call("attn_fwd_causal_mla", q, k, v, q_descale, k_descale, v_descale, softmax_scale, out, lse)
+
+
+def attn_fwd_causal_fp8_debug(q, k, v, q_descale, k_descale, v_descale, softmax_scale=None):
+    """Test hook: FP8 attention (d_qk 128 or 192) that also returns the per-(row, 64-key block)
+    scale exponents and the probability codes the kernel formed (255 / 0 where untouched)."""
+    B, S, H, _ = q.shape
+    dbg_o = torch.full((B * H * S, S // 64), 255, dtype=torch.uint8, device=q.device)
+    dbg_c = torch.zeros((B * H * S, S), dtype=torch.uint8, device=q.device)
+    out, lse = _fp8_call("attn_fwd_causal_fp8_debug", q, k, v, q_descale, k_descale, v_descale, softmax_scale,
+                         None, None, debug=(dbg_o, dbg_c))
+    return out, lse, dbg_o, dbg_c
+
+
+def attn_fwd_causal_bf16(q, k, v, softmax_scale=None, out=None, lse=None):
+    """BF16 causal attention, d_qk = d_v = 128.  Returns (out bf16, lse fp32)."""
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16:
+            raise TypeError("q, k, v must be bfloat16")
+    out, lse = _outputs(q, v, out, lse)
+    B, S, H, dqk, dv = _meta(q, k, v, out, lse)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(dqk)
+    rc = lib().attn_fwd_causal_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), float(softmax_scale),
+                                    B, H, S, dqk, dv, _stream())
+    _check("attn_fwd_causal_bf16", rc)
+    return out, lse
+
+
+def quantize_e4m3(x, workspace=None):
+    """Per-tensor power-of-two e4m3 quantisation of a float32 GPU tensor.
+
+    Returns (codes as float8_e4m3fn with x's shape, descale as a 1-element float32 tensor)."""
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise TypeError("x must be a contiguous float32 GPU tensor")
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    descale = torch.empty(1, dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(1, dtype=torch.int32, device=x.device)
+    rc = lib().attn_quantize_e4m3(_ptr(x), x.numel(), _ptr(codes), _ptr(descale), _ptr(workspace), _stream())
+    _check("attn_quantize_e4m3", rc)
+    return codes.view(torch.float8_e4m3fn), descale
+
+
+def round_bf16(x):
+    """fp32 -> bf16, round to nearest even, on the GPU."""
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise TypeError("x must be a contiguous float32 GPU tensor")
+    out = torch.empty(x.shape, dtype=torch.int16, device=x.device)
+    _check("attn_round_bf16", lib().attn_round_bf16(_ptr(x), x.numel(), _ptr(out), _stream()))
+    return out.view(torch.bfloat16)
+
+
+def default_grid(B, H, S, num_cu):
+    return lib().attn_default_grid(B, H, S, num_cu)
+
+
+def schedule(B, H, S, grid):
+    """Execution-order (workgroup, b, h, tile) records of the persistent grid (host only)."""
+    import numpy as np
+    T = S // 256
+    rec = np.zeros((B * H * T, 4), dtype=np.int32)
+    n = lib().attn_schedule(B, H, S, grid, ctypes.c_void_p(rec.ctypes.data), rec.shape[0])
+    if n < 0:
+        raise AttnError("attn_schedule", int(n))
+    return rec[:n]
+
+
+def flops(B, H, S, dqk, dv):
+    """Causal forward FLOP count F = B H S^2 (d_qk + d_v) (paper Sec. II-B, Eq. 1)."""
+    return float(B) * H * S * S * (dqk + dv)

@@ -1,0 +1,152 @@
+// Shared pieces of the causal attention forward kernels for gfx950 (CDNA4).
+//
+// Work decomposition, LDS layouts and MFMA operand types.  The method follows
+// "ZYFA: Speed and Accuracy of FP8 FlashAttention on AMD CDNA4" (Anthony et al.):
+// Sec. II-B (tiled causal attention), Sec. IV-A (workgroup structure, KQ^T
+// orientation, causal pairing, persistent grid, chiplet placement).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cfa {
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// A workgroup owns a tile of 256 query rows; each of its 8 waves owns 32 rows
+// (two waves per SIMD).  Keys stream through LDS in blocks of 128.
+constexpr int kTileRows = 256;
+constexpr int kWaves = 8;
+constexpr int kWaveRows = 32;
+constexpr int kThreads = 512;
+constexpr int kBlockKeys = 128;
+constexpr int kXcds = 8;
+
+// ---------------------------------------------------------------------------
+// Work decomposition (Sec. IV-A, "Causal pairing" and "Chiplet placement").
+// Per (b, h) there are T = S / 256 query tiles.  Work item j of a head runs tile
+// j and then tile T-1-j, so every item covers T+1 key steps of 256; when T is odd
+// the middle tile runs alone.  Items are numbered head-major, pairs contiguous:
+//   item = (b * H + h) * P + j,  P = ceil(T / 2).
+// A persistent grid of G workgroups walks the items with stride G.  The hardware
+// dispatches workgroup i to XCD i mod 8; the remap below gives each XCD a run of
+// consecutive logical ids, so consecutive pairs of one head share an L2.
+struct Schedule {
+  int T;          // tiles per head
+  int P;          // items per head
+  int64_t items;  // B * H * P
+};
+
+__host__ __device__ inline Schedule make_schedule(int B, int H, int S) {
+  Schedule s;
+  s.T = S / kTileRows;
+  s.P = (s.T + 1) / 2;
+  s.items = (int64_t)B * H * s.P;
+  return s;
+}
+
+// Bijection from the dispatch index to a logical index, for any grid size G:
+// XCD x holds n_x = G/8 + (x < G%8) workgroups and takes logical ids
+// [x*(G/8) + min(x, G%8), ... + n_x).
+__host__ __device__ inline int xcd_logical(int bid, int grid) {
+  const int per = grid / kXcds, rem = grid % kXcds;
+  const int x = bid % kXcds, idx = bid / kXcds;
+  return x * per + (x < rem ? x : rem) + idx;
+}
+
+__host__ __device__ inline void decode_item(int64_t item, int H, int P, int& b, int& h, int& j) {
+  const int64_t bh = item / P;
+  j = (int)(item - bh * P);
+  b = (int)(bh / H);
+  h = (int)(bh - (int64_t)b * H);
+}
+
+// ---------------------------------------------------------------------------
+// Key order inside a 32-key sub-tile.  The score MFMA computes S^T = K Q^T, so
+// lane l of a wave holds the scores of query l%32 (Sec. IV-A: max and sum need
+// one exchange between the two lanes of a query, the rescale one scalar per
+// lane).  Row i of the K operand is loaded from key pi(i) of the sub-tile; with
+// that order, lane half hh = l/32 holds keys 16*hh + r (r = 0..15) of each FP8
+// sub-tile in accumulator order, which is exactly the byte order the PV MFMA
+// needs for the probabilities, and the matching V^T operand is two contiguous
+// 16-byte LDS reads.
+__host__ __device__ constexpr int key_perm_fp8(int i) {
+  return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);
+}
+// BF16 (32x32x16 MFMA, 8 keys per lane half): lane half hh holds keys
+// 16*(r/8) + 8*hh + r%8.
+__host__ __device__ constexpr int key_perm_bf16(int i) {
+  return 16 * (i >> 4) + 8 * ((i >> 2) & 1) + 4 * ((i >> 3) & 1) + (i & 3);
+}
+
+// ---------------------------------------------------------------------------
+// LDS layouts (16-byte groups XOR-swizzled so MFMA operand reads and staging
+// writes are free of bank conflicts).
+//
+// FP8 K block: d_qk/64 planes of [128 keys][64 B]; plane stride 8192+64 B.
+constexpr int kFp8KPlane = 8192 + 64;
+__device__ __forceinline__ int fp8_k_off(int plane, int row, int grp) {
+  const int f = ((row >> 1) & 1) | (((row >> 4) & 1) << 1);
+  return plane * kFp8KPlane + row * 64 + ((grp ^ f) << 4);
+}
+// FP8 V^T block: [128 d][128 keys] bytes.
+__device__ __forceinline__ int fp8_vt_off(int d, int grp) {
+  const int f = (d & 7) ^ ((d >> 3) & 7);
+  return d * 128 + ((grp ^ f) << 4);
+}
+// BF16 K block: [128 keys][256 B].
+__device__ __forceinline__ int bf16_k_off(int row, int grp) {
+  const int f = (row & 3) | (((row >> 3) & 1) << 2);
+  return row * 256 + ((grp ^ f) << 4);
+}
+// BF16 V^T block: [128 d][128 keys x 2 B].
+__device__ __forceinline__ int bf16_vt_off(int d, int grp) {
+  const int f = (d & 7) ^ ((d >> 3) & 7);
+  return d * 256 + ((grp ^ f) << 4);
+}
+
+// byte permute: result byte k = sel byte k indexing {lo bytes 0-3, hi bytes 4-7}
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// 4x4 byte transpose: r[i] holds bytes (key i; d 0..3) -> s[e] holds (d e; keys 0..3).
+__device__ __forceinline__ void transpose4x4_u8(const uint32_t r[4], uint32_t s[4]) {
+  const uint32_t t0 = perm(r[1], r[0], 0x05010400u);
+  const uint32_t t1 = perm(r[1], r[0], 0x07030602u);
+  const uint32_t t2 = perm(r[3], r[2], 0x05010400u);
+  const uint32_t t3 = perm(r[3], r[2], 0x07030602u);
+  s[0] = perm(t2, t0, 0x05040100u);
+  s[1] = perm(t2, t0, 0x07060302u);
+  s[2] = perm(t3, t1, 0x05040100u);
+  s[3] = perm(t3, t1, 0x07060302u);
+}
+
+// value exchange between lane l and lane l^32 (gfx950 v_permlane32_swap).
+__device__ __forceinline__ float max_with_partner(float x) {
+  const uint32_t u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_with_partner(float x) {
+  const uint32_t u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fmax3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite here).
+__device__ __forceinline__ uint32_t bf16_bits_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return bf16_bits_rne(lo) | (bf16_bits_rne(hi) << 16);
+}
+
+}  // namespace cfa

@@ -1,0 +1,123 @@
+/*
+ * attn_fwd_causal.h -- C ABI of the causal attention forward (prefill) library for
+ * AMD Instinct MI355X (gfx950, CDNA4): libattn_fwd_causal.so.
+ *
+ * The operation is causal softmax attention, "ZYFA: Speed and Accuracy of FP8
+ * FlashAttention on AMD CDNA4" (Anthony, Bikshandi, Medepalli, Ebert), Sec. II-B:
+ *     O = softmax(c Q K^T + M) V,   M the causal mask (query i sees keys 0..i),
+ * with the log-sum-exp of every row of scores, for one (batch, head) at a time over
+ * B batches and H heads.  Supported configurations follow the paper's Table VI:
+ * causal forward only, equal query and key lengths S (a multiple of 256),
+ * multi-head attention, BF16 or e4m3 operands with one fp32 scale per tensor,
+ * BF16 output and fp32 LSE.
+ *
+ * Layout (all tensors dense, row-major):
+ *   q, k : [B][S][H][d_qk]   (BSHD, the (batch, seqlen, heads, headdim) order)
+ *   v    : [B][S][H][d_v]
+ *   out  : [B][S][H][d_v]    bf16
+ *   lse  : [B][H][S]         fp32, natural log of sum_j exp(c q_i.k_j) over visible
+ *                            keys (for FP8, of the rounded probabilities; Sec. IV-B3)
+ * e4m3 is the OCP "fn" variant (bias 7, max 448, no infinities), not FNUZ.
+ *
+ * Memory and ownership: every pointer is a device pointer owned by the caller;
+ * the library allocates nothing and keeps no pointer after a call returns.
+ * q, k, v, out must be 16-byte aligned, lse 4-byte aligned.
+ *
+ * Execution: calls are asynchronous on `stream` (a hipStream_t; NULL = the
+ * default stream) and never synchronise.  All functions are reentrant.  The
+ * attention kernels use a static work partition and no atomics, so results are
+ * bitwise identical from run to run (Sec. VI-B, Table XII property).
+ *
+ * Errors: arguments are validated on the host before any device call, and
+ * nothing is launched when a check fails.  A call with B, H or S equal to zero
+ * is a no-op that returns ATTN_OK.  Launch failures map to ATTN_ERR_LAUNCH.
+ * NaN or infinite inputs are not errors but are unsupported (outputs undefined).
+ */
+#ifndef ATTN_FWD_CAUSAL_H
+#define ATTN_FWD_CAUSAL_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = -1,   /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = -2,  /* negative size, S not a multiple of 256, or wrong head dims */
+  ATTN_ERR_ALIGN = -3,  /* pointer misaligned */
+  ATTN_ERR_RANGE = -4,  /* a tensor has 2^31 elements or more */
+  ATTN_ERR_ARG = -5,    /* a scale is not finite and positive, or a bad size argument */
+  ATTN_ERR_LAUNCH = -6, /* the kernel launch failed (hipGetLastError) */
+  ATTN_ERR_DEVICE = -7  /* no usable device / device query failed */
+} attn_status;
+
+/* FP8 causal attention at head dimension 128 with lean P.
+ * Paper Sec. IV-B1 (Eq. 2: each probability's e4m3 code from one multiply-add and
+ * an integer conversion), Sec. IV-B2 (per-64-key-block power-of-two scaling undone
+ * by the scaled PV MFMA), Sec. IV-B3 (row sum of the rounded probabilities),
+ * Sec. II-C (per-tensor scales folded into the score scale and the output).
+ * q, k, v: e4m3 codes; *_descale: the fp32 factors that map codes back to values
+ * (value = decoded code * descale); softmax_scale: c (e.g. 1/sqrt(128)).
+ * d_qk and d_v must both be 128. */
+int attn_fwd_causal_fp8(const void* q, const void* k, const void* v, void* out, float* lse, float q_descale,
+                        float k_descale, float v_descale, float softmax_scale, int B, int H, int S, int d_qk,
+                        int d_v, void* stream);
+
+/* BF16 causal attention at head dimension 128 (paper Sec. II-B, Sec. IV-A and
+ * IV-D: BF16 operands, fp32 softmax with the scale applied to the fp32 scores).
+ * q, k, v: bf16 bit patterns.  d_qk and d_v must both be 128. */
+int attn_fwd_causal_bf16(const void* q, const void* k, const void* v, void* out, float* lse,
+                         float softmax_scale, int B, int H, int S, int d_qk, int d_v, void* stream);
+
+/* FP8 causal attention at the MLA prefill shape, d_qk = 192 and d_v = 128, with
+ * exact P (paper Sec. IV-B1: the exponential and an e4m3 conversion per
+ * probability; Sec. IV intro: the MLA-shaped kernel keeps exact P), plus the
+ * block scaling and rounded-sum normaliser of Sec. IV-B2/B3.  Arguments as for
+ * attn_fwd_causal_fp8; d_qk must be 192 and d_v 128. */
+int attn_fwd_causal_mla(const void* q, const void* k, const void* v, void* out, float* lse, float q_descale,
+                        float k_descale, float v_descale, float softmax_scale, int B, int H, int S, int d_qk,
+                        int d_v, void* stream);
+
+/* Per-tensor power-of-two e4m3 quantiser (paper Sec. V-E, footnote 17): finds
+ * amax = max |x|, takes the largest 2^k with amax * 2^k <= 448 (k clamped to
+ * [-126, 126], k = 0 when amax = 0), writes codes[i] = e4m3_rne(x[i] * 2^k) and
+ * *descale = 2^-k.  x: n fp32 values (16-byte aligned); codes: n bytes (4-byte
+ * aligned); descale: one device float; workspace: one device uint32 that the
+ * call overwrites (do not share it between concurrent calls).  n >= 0. */
+int attn_quantize_e4m3(const float* x, int64_t n, uint8_t* codes, float* descale, uint32_t* workspace,
+                       void* stream);
+
+/* fp32 -> bf16 rounding to nearest even (the BF16 operands of the paper's Sec. V-D
+ * error measurement are the inputs rounded to BF16).  out: n uint16 bit patterns. */
+int attn_round_bf16(const float* x, int64_t n, uint16_t* out, void* stream);
+
+/* Test hooks.  Same computation as attn_fwd_causal_fp8 / attn_fwd_causal_mla, and
+ * in addition the kernel writes, for every (b, h, query row) and every block it
+ * processes, the block-scale exponent o of each 64-key block (dbg_o, [B*H*S][S/64]
+ * bytes) and the e4m3 code of every probability it forms (dbg_codes, [B*H*S][S]
+ * bytes; masked keys get code 0).  Entries of blocks the kernel skips are left
+ * untouched.  Limited to B*H*S*S <= 2^28. */
+int attn_fwd_causal_fp8_debug(const void* q, const void* k, const void* v, void* out, float* lse,
+                              float q_descale, float k_descale, float v_descale, float softmax_scale, int B,
+                              int H, int S, int d_qk, int d_v, uint8_t* dbg_o, uint8_t* dbg_codes, void* stream);
+
+/* Host-only helpers (no device call), for schedule inspection and tests.
+ * attn_default_grid: the persistent grid the attention entry points launch for a
+ *   problem on a device with num_cu compute units: min(num_cu, work items).
+ * attn_schedule: writes, in execution order, one (workgroup, b, h, tile) record of
+ *   four int32 per query tile that the grid of `grid` workgroups processes; returns
+ *   the number of records (B*H*S/256), or a negative attn_status if `cap` records do
+ *   not fit or the sizes are invalid. */
+int attn_default_grid(int B, int H, int S, int num_cu);
+int64_t attn_schedule(int B, int H, int S, int grid, int32_t* records, int64_t cap);
+
+/* Human-readable name of a status code. */
+const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_FWD_CAUSAL_H */

@@ -229,7 +229,7 @@ def emulate_fp8(q, k, v, *, dq: float, dk: float, dv: float, c: float, scheme: F
         "lse": np.empty(nrow, dtype=np.float64),
     }
     if debug:
-        res["o"] = np.empty((nrow, nblk), dtype=np.uint8)
+        res["o"] = np.full((nrow, nblk), 255, dtype=np.uint8)  # 255: block never visited
         res["codes"] = np.zeros((nrow, S), dtype=np.uint8)
         res["ymargin"] = np.full((nrow, S), np.inf, dtype=np.float32)
         res["omargin"] = np.full((nrow, nblk), np.inf, dtype=np.float32)

@@ -1,0 +1,163 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol, rejects
+bad arguments on the host before any device call, and its persistent-grid schedule
+covers every query tile exactly once with balanced work (paper Sec. IV-A, causal
+pairing).  Only invalid arguments are passed here, so nothing is ever launched."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bf16_causal_flashattention_amd as cfa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            txt = open(os.path.join(ROOT, "include", fn)).read()
+            names += re.findall(r"^\s*(?:int|int64_t|const char\s*\*)\s+(attn_\w+)\s*\(", txt, re.M)
+    return names
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) >= 9
+    L = ctypes.CDLL(cfa.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+FAKE = ctypes.c_void_p(1 << 20)       # never dereferenced: validation fails first
+MISALIGNED = ctypes.c_void_p((1 << 20) + 8)
+
+
+def _fp8(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, qd=1.0, kd=1.0, vd=1.0, sm=0.1, B=1, H=1, S=256,
+             dqk=128, dv=128)
+    a.update(kw)
+    return cfa.lib().attn_fwd_causal_fp8(a["q"], a["k"], a["v"], a["out"], a["lse"], a["qd"], a["kd"], a["vd"],
+                                         a["sm"], a["B"], a["H"], a["S"], a["dqk"], a["dv"], None)
+
+
+def _bf16(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, sm=0.1, B=1, H=1, S=256, dqk=128, dv=128)
+    a.update(kw)
+    return cfa.lib().attn_fwd_causal_bf16(a["q"], a["k"], a["v"], a["out"], a["lse"], a["sm"], a["B"], a["H"],
+                                          a["S"], a["dqk"], a["dv"], None)
+
+
+def _mla(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, qd=1.0, kd=1.0, vd=1.0, sm=0.1, B=1, H=1, S=256,
+             dqk=192, dv=128)
+    a.update(kw)
+    return cfa.lib().attn_fwd_causal_mla(a["q"], a["k"], a["v"], a["out"], a["lse"], a["qd"], a["kd"], a["vd"],
+                                         a["sm"], a["B"], a["H"], a["S"], a["dqk"], a["dv"], None)
+
+
+@pytest.mark.parametrize("call", [_fp8, _bf16, _mla])
+def test_validation_errors(call):
+    assert call(q=None) == -1
+    assert call(out=None) == -1
+    assert call(S=300) == -2
+    assert call(S=128) == -2
+    assert call(S=-256) == -2
+    assert call(B=-1) == -2
+    assert call(dv=64) == -2
+    assert call(q=MISALIGNED) == -3
+    assert call(out=MISALIGNED) == -3
+    assert call(lse=ctypes.c_void_p((1 << 20) + 2)) == -3
+    assert call(B=1, H=1 << 14, S=1 << 20) == -4
+    assert call(sm=float("nan")) == -5
+    assert call(sm=0.0) == -5
+    assert call(sm=float("inf")) == -5
+
+
+@pytest.mark.parametrize("call", [_fp8, _mla])
+def test_validation_errors_descales(call):
+    assert call(qd=0.0) == -5
+    assert call(kd=-1.0) == -5
+    assert call(vd=float("nan")) == -5
+
+
+def test_head_dims_per_entry_point():
+    assert _fp8(dqk=192) == -2
+    assert _mla(dqk=128) == -2
+    assert _bf16(dqk=192) == -2
+
+
+@pytest.mark.parametrize("call", [_fp8, _bf16, _mla])
+def test_empty_problem_is_noop(call):
+    # zero-sized problems return ok without touching the device, even with null pointers
+    assert call(B=0, q=None, k=None, v=None, out=None) == 0
+    assert call(H=0, q=None, k=None, v=None, out=None) == 0
+    assert call(S=0, q=None, k=None, v=None, out=None) == 0
+
+
+def test_prep_validation():
+    L = cfa.lib()
+    assert L.attn_quantize_e4m3(FAKE, -1, FAKE, FAKE, FAKE, None) == -5
+    assert L.attn_quantize_e4m3(None, 16, FAKE, FAKE, FAKE, None) == -1
+    assert L.attn_quantize_e4m3(FAKE, 16, FAKE, None, FAKE, None) == -1
+    assert L.attn_quantize_e4m3(MISALIGNED, 16, FAKE, FAKE, FAKE, None) == -3
+    assert L.attn_round_bf16(FAKE, -3, FAKE, None) == -5
+    assert L.attn_round_bf16(None, 3, FAKE, None) == -1
+    assert L.attn_round_bf16(FAKE, 0, None, None) == 0
+
+
+def test_status_strings():
+    L = cfa.lib()
+    for c in range(-7, 1):
+        assert L.attn_status_string(c)
+    assert b"unknown" in L.attn_status_string(-99)
+
+
+@pytest.mark.parametrize("B,H,S,grid", [(1, 1, 256, 1), (1, 32, 32768, 256), (2, 3, 1280, 7), (1, 16, 32768, 256),
+                                        (4, 5, 2048, 13), (1, 1, 768, 256), (3, 2, 2560, 256)])
+def test_schedule_covers_every_tile_once(B, H, S, grid):
+    T = S // 256
+    g = min(grid, cfa.default_grid(B, H, S, grid))
+    rec = cfa.schedule(B, H, S, g)
+    assert rec.shape[0] == B * H * T
+    seen = np.zeros((B, H, T), dtype=np.int64)
+    np.add.at(seen, (rec[:, 1], rec[:, 2], rec[:, 3]), 1)
+    assert np.all(seen == 1)
+    # work per workgroup in 256-key steps: tile t costs t+1; pairs (j, T-1-j) cost T+1
+    work = np.zeros(g, dtype=np.int64)
+    np.add.at(work, rec[:, 0], rec[:, 3] + 1)
+    items = B * H * ((T + 1) // 2)
+    per = math.ceil(items / g)
+    assert work.max() <= per * (T + 1)
+    # consecutive tiles of a workgroup alternate j, T-1-j within one head
+    for wg in range(min(g, 4)):
+        r = rec[rec[:, 0] == wg]
+        i = 0
+        while i < len(r):
+            if r[i, 3] == T - 1 - r[i, 3]:  # middle tile of an odd T runs alone
+                i += 1
+                continue
+            assert r[i + 1, 3] == T - 1 - r[i, 3] and r[i + 1, 1] == r[i, 1] and r[i + 1, 2] == r[i, 2]
+            i += 2
+
+
+def test_xcd_remap_is_contiguous_per_chiplet():
+    # workgroup i runs on chiplet i % 8; its first item should be a contiguous run per chiplet
+    B, H, S, g = 1, 32, 32768, 256
+    rec = cfa.schedule(B, H, S, g)
+    first = {}
+    for wg, b, h, t in rec:
+        if wg not in first:
+            first[wg] = (h, min(t, S // 256 - 1 - t))
+    for x in range(8):
+        heads = {first[wg][0] for wg in range(x, g, 8)}
+        assert len(heads) == 1  # 32 workgroups of one chiplet start on one head
+
+
+def test_default_grid():
+    assert cfa.default_grid(1, 32, 32768, 256) == 256
+    assert cfa.default_grid(1, 1, 256, 256) == 1
+    assert cfa.default_grid(1, 1, 300, 256) == -2
