@@ -1,0 +1,282 @@
+"""Benchmark: causal attention forward (prefill) on one MI355X.
+
+Headline: FP8 e4m3 causal prefill, B=1, H=32, S=32768, d_qk=d_v=128 (lean P), reported
+as TFLOP/s with F = B H S^2 (d_qk + d_v) and as a fraction of the dense FP8 MFMA peak.
+Timing is kernel-only as in "ZYFA: Speed and Accuracy of FP8 FlashAttention on AMD
+CDNA4", Sec. V-B: warm-up launches, then the mean over K launches measured with HIP
+events recorded on the launch stream; the per-tensor quantisation of the inputs runs
+before the timed region (Sec. V-E) and is timed on its own.  The line also carries
+the BF16 kernel at the same shape, the MLA-shaped FP8 kernel (B=1, H=16, S=32768,
+192/128), the activation-like FP8 input (B=1, H=32, S=16384) and the oracle timed on
+host cores over a bounded sample of the headline workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only-headline] [--no-cpu-baseline]
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import subprocess
+import sys
+import threading
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "causal prefill TFLOPS and % of FP8/BF16 MFMA peak, S=32K, d=128 and MLA 192/128"
+PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}  # MI355X dense MFMA peaks at 2.4 GHz
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fp8_attn_B1_H32_S32768_d128_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "bf16_causal_flashattention_amd", "csrc", "attn_fp8.hip")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def flops(B, H, S, dqk, dv):
+    return float(B) * H * S * S * (dqk + dv)
+
+
+def fp8_hbm_bytes(B, H, S, dqk, dv, elem=1):
+    """Algorithmic HBM bytes of one call: read Q, K, V once, write O (bf16) and LSE (fp32)."""
+    return B * S * H * (2 * dqk + dv) * elem + B * S * H * dv * 2 + B * H * S * 4
+
+
+def src_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+class ClockSampler:
+    """Samples the shader clock with amd-smi while the timed window runs (best effort)."""
+
+    def __init__(self):
+        self.samples = []
+        self._stop = threading.Event()
+        self._t = None
+
+    def _one(self):
+        try:
+            r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"], capture_output=True, text=True,
+                               timeout=5)
+            data = json.loads(r.stdout)
+            if isinstance(data, list):
+                data = data[0]
+            clk = data.get("clock", data)
+            vals = []
+            for key, val in clk.items():
+                if key.startswith("gfx") and isinstance(val, dict):
+                    cur = val.get("clk", val.get("cur_clk"))
+                    if isinstance(cur, dict):
+                        cur = cur.get("value")
+                    if cur not in (None, "N/A"):
+                        vals.append(float(cur))
+            if vals:
+                self.samples.append(min(vals))
+        except Exception:
+            pass
+
+    def _run(self):
+        while not self._stop.is_set():
+            self._one()
+            self._stop.wait(0.25)
+
+    def __enter__(self):
+        self._t = threading.Thread(target=self._run, daemon=True)
+        self._t.start()
+        return self
+
+    def __exit__(self, *a):
+        self._stop.set()
+        self._t.join(timeout=10)
+
+    def median(self):
+        return float(np.median(self.samples)) if self.samples else None
+
+
+def time_launches(torch, fn, warmup, steps):
+    """Mean device time per launch (ms) over `steps` launches, HIP events on the launch stream."""
+    for _ in range(warmup):
+        fn()
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def prep_fp8(torch, cfa, synth_fn, B, S, H, dqk, dv, seed):
+    import synth
+    q, k, v = synth_fn(B, S, H, dqk, dv, seed)
+    dev = torch.device("cuda:0")
+    tens = [torch.from_numpy(x).to(dev) for x in (q, k, v)]
+    del q, k, v
+    out = [cfa.quantize_e4m3(t) for t in tens]
+    torch.cuda.synchronize()
+    prep = lambda: [cfa.quantize_e4m3(t) for t in tens]
+    return tens, [o[0] for o in out], [float(o[1].item()) for o in out], prep
+
+
+def run_fp8(torch, cfa, kind, synth_fn, B, H, S, dqk, warmup, steps, seed=0):
+    log(f"{kind} B={B} H={H} S={S} d_qk={dqk}: generating inputs")
+    tens, codes, ds, prep = prep_fp8(torch, cfa, synth_fn, B, S, H, dqk, 128, seed)
+    qg, kg, vg = codes
+    out = torch.empty((B, S, H, 128), dtype=torch.bfloat16, device="cuda:0")
+    lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda:0")
+    entry = cfa.attn_fwd_causal_fp8 if dqk == 128 else cfa.attn_fwd_causal_mla
+    fn = lambda: entry(qg, kg, vg, ds[0], ds[1], ds[2], out=out, lse=lse)
+    with ClockSampler() as clk:
+        ms = time_launches(torch, fn, warmup, steps)
+    prep_ms = time_launches(torch, prep, 2, 5)
+    log(f"{kind} B={B} H={H} S={S} d_qk={dqk}: {ms:.4f} ms/launch")
+    del tens
+    F = flops(B, H, S, dqk, 128)
+    return {"ms": ms, "tflops": F / (ms * 1e-3) / 1e12, "prep_ms": prep_ms, "sclk_mhz": clk.median(),
+            "bytes": fp8_hbm_bytes(B, H, S, dqk, 128, 1)}
+
+
+def run_bf16(torch, cfa, B, H, S, warmup, steps, seed=0):
+    import synth
+    log(f"bf16 B={B} H={H} S={S}: generating inputs")
+    q, k, v = synth.gaussian(B, S, H, 128, 128, seed)
+    dev = torch.device("cuda:0")
+    tens = [torch.from_numpy(x).to(dev) for x in (q, k, v)]
+    del q, k, v
+    qg, kg, vg = (cfa.round_bf16(t) for t in tens)
+    out = torch.empty((B, S, H, 128), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    fn = lambda: cfa.attn_fwd_causal_bf16(qg, kg, vg, out=out, lse=lse)
+    with ClockSampler() as clk:
+        ms = time_launches(torch, fn, warmup, steps)
+    F = flops(B, H, S, 128, 128)
+    log(f"bf16 B={B} H={H} S={S}: {ms:.4f} ms/launch")
+    return {"ms": ms, "tflops": F / (ms * 1e-3) / 1e12, "sclk_mhz": clk.median()}
+
+
+def cpu_baseline(B, H, S, dqk, budget_s=20.0, seed=0):
+    """The oracle's FP8 emulation (mirror mode) timed on host cores over a bounded sample
+    of the headline workload: 32-row groups at seeded positions until ~budget_s of work."""
+    import oracle
+    import synth
+    q, k, v = synth.gaussian(B, S, H, dqk, 128, seed)
+    t0 = time.time()
+    (qc, dq), (kc, dk), (vc, dv) = (oracle.quantize_e4m3(x) for x in (q, k, v))
+    del q, k, v
+    rng = np.random.default_rng(seed + 1)
+    c = 1.0 / math.sqrt(dqk)
+    total_f, total_t, ngroups = 0.0, 0.0, 0
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    log(f"cpu baseline: oracle quantised inputs in {time.time() - t0:.1f} s, sampling for ~{budget_s:.0f} s")
+    while total_t < budget_s and ngroups < 4096:
+        n = threads
+        groups = np.stack([rng.integers(0, B, n), rng.integers(0, H, n), rng.integers(0, S // 32, n) * 32], axis=1)
+        t1 = time.perf_counter()
+        oracle.emulate_fp8(qc, kc, vc, dq=dq, dk=dk, dv=dv, c=c, groups=groups.astype(np.int64))
+        total_t += time.perf_counter() - t1
+        rows = oracle.group_rows(groups, 32)
+        total_f += float(np.sum(2.0 * (rows[:, 2] + 1) * (dqk + 128)))
+        ngroups += n
+    return {"value": total_f / total_t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"FP8 scheme emulation (mirror mode) of {ngroups} seeded 32-row groups of the "
+                      f"B={B} H={H} S={S} d={dqk} workload, {total_t:.1f} s of CPU time; F counts the causal "
+                      f"half of each sampled row; host quantisation ({time.time() - t0 - total_t:.1f} s) excluded"}
+
+
+def traffic_entry():
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        if t.get("kernel_src_sha256_16") != src_hash(KERNEL_SRC):
+            return None  # kernel changed since the counters were taken
+        return t.get("bytes_per_launch")
+    except Exception:
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--only-headline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads shard across GPUs with no communication; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import bf16_causal_flashattention_amd as cfa
+    cfa.lib()  # fail loudly when the HIP library is missing
+
+    B, H, S, D = 1, 32, 32768, 128
+    head = run_fp8(torch, cfa, "fp8", synth.gaussian, B, H, S, D, args.warmup, args.steps)
+    F = flops(B, H, S, D, D)
+    achieved = F / (head["ms"] * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": round(head["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)",
+        "data": "synthetic: q, k, v ~ N(0,1) fp32 from seed 0, quantised per tensor to e4m3 on the GPU",
+        "config": {"workload": "FP8 causal prefill B=1 H=32 S=32768 d_qk=d_v=128, lean P", "B": B, "H": H,
+                   "S": S, "d_qk": D, "d_v": D, "parallelism": "single GPU"},
+        "pct_fp8_peak": round(100 * head["tflops"] / PEAK_TFLOPS["fp8"], 2),
+        "sclk_mhz_median": head["sclk_mhz"],
+        "prep_ms_qkv_quantise": round(head["prep_ms"], 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["fp8"],
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["fp8"], 4),
+                     "traffic": traffic_entry(),
+                     "algorithmic_hbm_bytes": head["bytes"],
+                     "hbm_gbs_at_algorithmic_bytes": round(head["bytes"] / (head["ms"] * 1e-3) / 1e9, 1)},
+    }
+    if not args.only_headline:
+        also = {}
+        wb, sb = max(3, args.warmup // 4), max(5, args.steps // 4)
+        r = run_bf16(torch, cfa, 1, 32, 32768, wb, sb)
+        also["bf16_B1_H32_S32768_d128"] = {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4),
+                                           "pct_bf16_peak": round(100 * r["tflops"] / PEAK_TFLOPS["bf16"], 2),
+                                           "sclk_mhz_median": r["sclk_mhz"]}
+        for s in (4096, 8192, 16384):
+            r = run_bf16(torch, cfa, 1, 32, s, wb, sb)
+            also[f"bf16_B1_H32_S{s}_d128"] = {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4)}
+            r = run_fp8(torch, cfa, "fp8", synth.gaussian, 1, 32, s, 128, wb, sb)
+            also[f"fp8_B1_H32_S{s}_d128"] = {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4)}
+        r = run_fp8(torch, cfa, "mla", synth.gaussian, 1, 16, 32768, 192, wb, sb)
+        also["mla_fp8_B1_H16_S32768_192_128"] = {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4),
+                                                  "pct_fp8_peak": round(100 * r["tflops"] / PEAK_TFLOPS["fp8"], 2)}
+        r = run_fp8(torch, cfa, "fp8", synth.activation_like, 1, 32, 16384, 128, wb, sb)
+        also["fp8_activation_like_B1_H32_S16384_d128"] = {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4),
+                                                          "sclk_mhz_median": r["sclk_mhz"]}
+        result["also"] = also
+        result["fp8_over_bf16_speedup_S32768"] = round(head["tflops"] / also["bf16_B1_H32_S32768_d128"]["tflops"], 3)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(B, H, S, D, budget_s=args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
