@@ -8,10 +8,24 @@
 //                      exact P: FMA + exp2 + e4m3 conversion (MLA shape, d_qk = 192);
 //   Sec. IV-B2         per (query, 64-key block) power-of-two scale 2^o, removed by the
 //                      E8M0 operand scale of the PV MFMA;
-//   Sec. IV-B3         row sum of the rounded probabilities on the matrix unit.
+//   Sec. IV-B3         row sum of the rounded probabilities on the matrix unit;
+//   Sec. IV-C, Fig. 6  two-wave ping-pong: the two waves of a SIMD alternate between an
+//                      MFMA phase (row sums, S^T of the next block, PV of the current
+//                      block, next block's maximum and rescale decision) and a softmax
+//                      phase (the probability codes), with a workgroup barrier per phase.
+//
+// Schedule per 256-row tile with nb 128-key blocks.  Group g = wave / 4 (one wave of
+// each group per SIMD).  Group 1 runs one phase behind group 0:
+//   group 0:  M_pro S_pro M_0 S_0 M_1 S_1 ... M_{nb-1} S_{nb-1} idle
+//   group 1:  idle  M_pro S_pro M_0 S_0 ... M_{nb-1} S_{nb-1}
+// M_i: row sums of P(i); S(i+1) = K(i+1) Q^T; O += V(i)^T P(i); max of S(i+1), lazy
+//      decision, o(i+1).   S_i: P(i+1) from S(i+1).
+// Staging (global -> registers in M_i, registers -> LDS in S_i): group 0 stages K(i+2),
+// group 1 stages V(i+2)^T.  With two LDS slots per operand every write lands one phase
+// after the slot's last read and at least one phase before its first read.
 //
 // fp32 arithmetic (the order below is part of the contract with the test oracle):
-//   cp   = fp32(c * dq * dk * log2 e), scores s are fp32 MFMA sums of exact products
+//   cp   = fp32(c * dq * dk * log2 e), scores s are fp32 MFMA sums
 //   t    = s * cp;  M = max(m, max t);  lazy: keep m unless some row of the wave
 //          grows by >= tau; rescale factor 2^(m - M)
 //   o    = clamp(floor(m - b), 0, 127), b = max t over the 64-key block
@@ -31,51 +45,75 @@ constexpr int kSigma = 6;          // probability shift 2^6 (Sec. IV-B1)
 constexpr float kBeta = 0.35f;     // lean-P bias (Sec. IV-B1, Eq. 2)
 constexpr float kLn2 = 0.69314718055994530942f;
 
+// LDS: two K slots then two V^T slots.
+//   K slot: row 32*(key/32) + kinv(key%32) holds key `key`, row stride DQK + 16 bytes, so
+//           lane i of a wave reads row 32u + i, which holds key 32u + key_perm_fp8(i).
+//   V^T slot: row d (128 rows, stride 144 bytes) holds V[key][d] for the block's 128 keys,
+//           16-byte key groups stored with bits 0 and 1 of the group index swapped, so a
+//           lane's 32 PV operand bytes (keys 64n+16hh+j and 64n+32+16hh+j) are contiguous.
 template <int DQK>
-struct Fp8Layout {
-  static constexpr int kKc = DQK / 64;                      // 64-wide k chunks of the score MFMA
-  static constexpr int kKBytes = kKc * kFp8KPlane;          // K block in LDS
-  static constexpr int kVtOff = kKBytes;                    // V^T block follows
-  static constexpr int kStage = kKBytes + 128 * 128;        // one K+V^T stage
-  static constexpr int kLds = 2 * kStage;                   // double buffered
-  static constexpr int kKChunks = 128 * DQK / 16;           // 16-byte chunks of a K block
-  static_assert(kKChunks % kThreads == 0, "K chunks per thread");
-  static constexpr int kKPerThread = kKChunks / kThreads;  // == kKc
+struct Fp8Lds {
+  static constexpr int kKc = DQK / 64;
+  static constexpr int kKStride = DQK + 16;
+  static constexpr int kKSlot = 128 * kKStride;
+  static constexpr int kVStride = 144;
+  static constexpr int kVSlot = 128 * kVStride;
+  static constexpr int kVBase = 2 * kKSlot;
+  static constexpr int kBytes = 2 * kKSlot + 2 * kVSlot;
+  static constexpr int kKChunksPerThread = 128 * DQK / 16 / 256;  // staged by 256 threads
 };
 
-__device__ __forceinline__ v8i cat8(v4i a, v4i b) {
-  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+__device__ __forceinline__ int kinv(int k) { return 8 * ((k >> 2) & 3) + 4 * (k >> 4) + (k & 3); }
+__device__ __forceinline__ int vt_group(int g) { return (g & 4) | ((g & 1) << 1) | ((g >> 1) & 1); }
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 template <int DQK, bool EXACT_P, bool DEBUG>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
-  using L = Fp8Layout<DQK>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[L::kLds];
+  using L = Fp8Lds<DQK>;
+  constexpr int KC = L::kKc;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[L::kBytes];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
+  const int grp = wave >> 2;  // 0: waves 0-3, 1: waves 4-7 (one of each per SIMD)
   const int S = a.S, H = a.H;
   const Schedule sch = make_schedule(a.B, H, S);
   const int logical = xcd_logical(blockIdx.x, gridDim.x);
 
-  // staging assignment (constant over blocks)
-  int k_row[L::kKPerThread], k_gg[L::kKPerThread];
+  const int krs = H * DQK;  // BSHD key row stride in bytes (tensor < 2^31 elements)
+  const int vrs = H * 128;
+
+  // per-lane LDS read bases
+  const int k_rd = l32 * L::kKStride + 32 * hh;
+  const int v_rd = L::kVBase + l32 * L::kVStride + 32 * hh;
+
+  // staging assignments: the 256 threads of group 0 stage K, those of group 1 stage V^T.
+  // Both use one register array and the same load code; only the LDS store differs.
+  constexpr int NST = L::kKChunksPerThread;  // 16-byte chunks per staging thread (>= 4)
+  const int st = tid & 255;
+  const bool stage_k = (grp == 0);
+  const int st_rs = stage_k ? krs : vrs;  // global row stride of the staged tensor
+  int st_goff[NST], k_soff[NST];
+  const int v_kg = st & 31, v_dc = st >> 5;  // V: keys 4kg..4kg+3, d 16dc..16dc+15
 #pragma unroll
-  for (int p = 0; p < L::kKPerThread; ++p) {
-    const int id = tid + kThreads * p;
-    k_row[p] = id / (DQK / 16);
-    k_gg[p] = id % (DQK / 16);
+  for (int p = 0; p < NST; ++p) {
+    const int id = st + 256 * p, key = id / (DQK / 16), gg = id % (DQK / 16);
+    st_goff[p] = stage_k ? key * krs + 16 * gg : (4 * v_kg + (p & 3)) * vrs + 16 * v_dc;
+    k_soff[p] = ((key & ~31) | kinv(key & 31)) * L::kKStride + 16 * gg;
   }
-  const int v_dc = tid & 15, v_kg = tid >> 4;
-  const int64_t krs = (int64_t)H * DQK;  // key row stride (bytes) in BSHD
-  const int64_t vrs = (int64_t)H * 128;
+  const int v_soff = L::kVBase + 16 * v_dc * L::kVStride + 16 * vt_group(v_kg >> 2) + 4 * (v_kg & 3);
 
   // row-sum selector (Sec. IV-B3): lane L of the 16x16x128 A operand is all ones
   // iff (L/16)%2 == ((L%16)/4)%2, so every lane receives the sum of its own query.
   const int sel_on = (((lane >> 4) & 1) == (((lane & 15) >> 2) & 1));
   const int selw = sel_on ? 0x38383838 : 0;
-  const v8i sel = {selw, selw, selw, selw, selw, selw, selw, selw};
   const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
+  const v16f zero16 = {};
 
   const float cp = a.cp;
   const float cp8 = 8.0f * cp;
@@ -83,9 +121,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
   for (int64_t item = logical; item < sch.items; item += gridDim.x) {
     int b, h, j;
     decode_item(item, H, sch.P, b, h, j);
-    const uint8_t* kbh = a.k + ((int64_t)b * S * H + h) * DQK;
-    const uint8_t* vbh = a.v + ((int64_t)b * S * H + h) * 128;
     const uint8_t* qbh = a.q + ((int64_t)b * S * H + h) * DQK;
+    const uint8_t* st_head = stage_k ? a.k + ((int64_t)b * S * H + h) * DQK : a.v + ((int64_t)b * S * H + h) * 128;
 
     for (int pass = 0; pass < 2; ++pass) {
       const int tile = pass == 0 ? j : sch.T - 1 - j;
@@ -94,197 +131,214 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
       const int qrow = row0 + l32;
       const int nb = 2 * tile + 2;                             // 128-key blocks
 
-      // Q^T operand of the score MFMA: lane holds Q[qrow][64c + 32hh .. +32]
-      v8i qop[L::kKc];
+      // ---------------------------------------------------------------- staging
+      v4i stg[NST];
+      auto stage_load = [&](int blk) {  // global -> registers for block blk
+        const uint8_t* base = st_head + (int64_t)(blk * kBlockKeys) * st_rs;
+#pragma unroll
+        for (int p = 0; p < NST; ++p)
+          if (p < 4 || stage_k) stg[p] = *(const v4i*)(base + st_goff[p]);
+      };
+      auto stage_store = [&](int blk) {  // registers -> LDS slot blk % 2
+        const int slot = blk & 1;
+        if (stage_k) {
+          uint8_t* sk = smem + slot * L::kKSlot;
+#pragma unroll
+          for (int p = 0; p < NST; ++p) *(v4i*)(sk + k_soff[p]) = stg[p];
+        } else {
+          uint8_t* sv = smem + slot * L::kVSlot + v_soff;
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {  // d 16dc + 4q4 .. +3
+            uint32_t r[4], t[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) r[i] = (uint32_t)stg[i][q4];
+            transpose4x4_u8(r, t);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) *(uint32_t*)(sv + (4 * q4 + e) * L::kVStride) = t[e];
+          }
+        }
+      };
+
+      // ---------------------------------------------------------------- per-wave state
+      v8i qop[KC];
       {
         const uint8_t* qp = qbh + (int64_t)qrow * krs + 32 * hh;
 #pragma unroll
-        for (int c = 0; c < L::kKc; ++c) {
-          const v4i x0 = *(const v4i*)(qp + 64 * c);
-          const v4i x1 = *(const v4i*)(qp + 64 * c + 16);
-          qop[c] = cat8(x0, x1);
-        }
+        for (int c = 0; c < KC; ++c) qop[c] = *(const v8i*)(qp + 64 * c);
       }
-
       v16f oacc[4];
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
-      float m = 0.f, l = 0.f;
+      for (int dt = 0; dt < 4; ++dt) oacc[dt] = zero16;
+      v16f sacc[4];  // scores of the next block
+      v8i pb[2];     // codes of the current block, per 64-key scale block
+      float m = 0.f, l = 0.f, fres = 1.f;
+      int o_cur[2] = {0, 0}, o_nxt[2] = {0, 0};
+      bool rescale = false;
 
-      v4i kreg[L::kKPerThread];
-      v2i vreg[4];
-      auto load_kv = [&](int key0) {
+      auto live = [&](int blk) { return blk * kBlockKeys <= row0 + kWaveRows - 1; };
+
+      // S^T(blk) = K(blk) Q^T into sacc
+      auto qk = [&](int blk) {
+        const uint8_t* sk = smem + (blk & 1) * L::kKSlot + k_rd;
 #pragma unroll
-        for (int p = 0; p < L::kKPerThread; ++p)
-          kreg[p] = *(const v4i*)(kbh + (int64_t)(key0 + k_row[p]) * krs + 16 * k_gg[p]);
+        for (int u = 0; u < 4; ++u) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          vreg[i] = *(const v2i*)(vbh + (int64_t)(key0 + 4 * v_kg + i) * vrs + 8 * v_dc);
-      };
-      auto store_kv = [&](int stage) {
-        uint8_t* sb = smem + stage * L::kStage;
-#pragma unroll
-        for (int p = 0; p < L::kKPerThread; ++p)
-          *(v4i*)(sb + fp8_k_off(k_gg[p] >> 2, k_row[p], k_gg[p] & 3)) = kreg[p];
-        uint32_t lo[4], hi[4], tlo[4], thi[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          lo[i] = (uint32_t)vreg[i][0];
-          hi[i] = (uint32_t)vreg[i][1];
-        }
-        transpose4x4_u8(lo, tlo);
-        transpose4x4_u8(hi, thi);
-        uint8_t* sv = sb + L::kVtOff;
-        const int grp = v_kg >> 2, within = 4 * (v_kg & 3);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          *(uint32_t*)(sv + fp8_vt_off(8 * v_dc + e, grp) + within) = tlo[e];
-          *(uint32_t*)(sv + fp8_vt_off(8 * v_dc + 4 + e, grp) + within) = thi[e];
+          for (int c = 0; c < KC; ++c) {
+            const v8i kop = *(const v8i*)(sk + 32 * u * L::kKStride + 64 * c);
+            sacc[u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop, qop[c], c == 0 ? zero16 : sacc[u], 0,
+                                                                       0, 0, 127, 0, 127);
+          }
         }
       };
-
-      load_kv(0);
-      store_kv(0);
-      __syncthreads();
-
-      for (int kb = 0; kb < nb; ++kb) {
-        const int key0 = kb * kBlockKeys;
-        const int cur = kb & 1;
-        if (kb + 1 < nb) load_kv(key0 + kBlockKeys);
-
-        if (key0 <= row0 + kWaveRows - 1) {  // else every key of the block is masked for this wave
-          const uint8_t* sk = smem + cur * L::kStage;
-          const uint8_t* sv = sk + L::kVtOff;
-          // ---- S^T = K Q^T for four 32-key sub-tiles
-          v16f sacc[4];
+      // mask, block maxima, running max with the lazy decision, exponents o for blk
+      auto max_step = [&](int blk, bool first) {
+        const int key0 = blk * kBlockKeys;
+        if (key0 + kBlockKeys - 1 > row0) {  // diagonal block: key key0+32u+16hh+r
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
+          for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[u][r] = 0.f;
-            const int row = 32 * u + key_perm_fp8(l32);
+            for (int r = 0; r < 16; ++r)
+              if (key0 + 32 * u + 16 * hh + r > qrow) sacc[u][r] = -INFINITY;
+        }
+        float bm[2];
 #pragma unroll
-            for (int c = 0; c < L::kKc; ++c) {
-              const v4i x0 = *(const v4i*)(sk + fp8_k_off(c, row, 2 * hh));
-              const v4i x1 = *(const v4i*)(sk + fp8_k_off(c, row, 2 * hh + 1));
-              sacc[u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cat8(x0, x1), qop[c], sacc[u], 0, 0, 0,
-                                                                         127, 0, 127);
+        for (int n = 0; n < 2; ++n) {
+          float x = fmaxf(sacc[2 * n][0], sacc[2 * n][1]);
+#pragma unroll
+          for (int r = 2; r < 16; r += 2) x = fmax3(x, sacc[2 * n][r], sacc[2 * n][r + 1]);
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) x = fmax3(x, sacc[2 * n + 1][r], sacc[2 * n + 1][r + 1]);
+          bm[n] = max_with_partner(x) * cp;
+        }
+        if (first) {
+          m = fmaxf(bm[0], bm[1]);
+        } else {
+          const float M = fmax3(m, bm[0], bm[1]);
+          rescale = __any((M - m) >= kTauFp8);
+          if (rescale) {
+            fres = __builtin_amdgcn_exp2f(m - M);
+            m = M;
+          }
+        }
+#pragma unroll
+        for (int n = 0; n < 2; ++n) o_nxt[n] = (int)fminf(fmaxf(floorf(m - bm[n]), 0.f), 127.f);
+      };
+      // probability codes of the scores in sacc (Sec. IV-B1)
+      auto codes = [&](int blk) {
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          if constexpr (!EXACT_P) {
+            const float cst = 8.0f * ((float)(kSigma + 7 + o_nxt[n]) - m) - kBeta;
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+              const int u = 2 * n + (w >> 2), r0 = 4 * (w & 3);
+              uint32_t x = 0;
+              x = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sacc[u][r0 + 0], cp8, cst), 0, x);
+              x = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sacc[u][r0 + 1], cp8, cst), 1, x);
+              x = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sacc[u][r0 + 2], cp8, cst), 2, x);
+              x = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sacc[u][r0 + 3], cp8, cst), 3, x);
+              pb[n][w] = (int)x;
             }
-          }
-          // ---- causal mask: lane half hh, sub-tile u, register r holds key key0+32u+16hh+r
-          if (key0 + kBlockKeys - 1 > row0) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-              for (int r = 0; r < 16; ++r)
-                if (key0 + 32 * u + 16 * hh + r > qrow) sacc[u][r] = -INFINITY;
-          }
-          // ---- block maxima (raw units) per 64-key scale block
-          float bmax[2];
-#pragma unroll
-          for (int n = 0; n < 2; ++n) {
-            float x = -INFINITY;
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) x = fmax3(x, sacc[2 * n][r], sacc[2 * n][r + 1]);
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) x = fmax3(x, sacc[2 * n + 1][r], sacc[2 * n + 1][r + 1]);
-            bmax[n] = max_with_partner(x);
-          }
-          const float tb0 = bmax[0] * cp, tb1 = bmax[1] * cp;
-          // ---- running max with lazy rescale (Sec. IV-A)
-          if (kb == 0) {
-            m = fmaxf(tb0, tb1);
           } else {
-            const float M = fmax3(m, tb0, tb1);
-            const int grow = (M - m) >= kTauFp8;
-            if (__any(grow)) {
-              const float f = __builtin_amdgcn_exp2f(m - M);
+            const float cst = (float)(kSigma + o_nxt[n]) - m;
 #pragma unroll
-              for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[dt][r] *= f;
-              l *= f;
-              m = M;
+            for (int w = 0; w < 8; ++w) {
+              const int u = 2 * n + (w >> 2), r0 = 4 * (w & 3);
+              const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[u][r0 + 0], cp, cst));
+              const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[u][r0 + 1], cp, cst));
+              const float p2 = __builtin_amdgcn_exp2f(fmaf(sacc[u][r0 + 2], cp, cst));
+              const float p3 = __builtin_amdgcn_exp2f(fmaf(sacc[u][r0 + 3], cp, cst));
+              int x = 0;
+              x = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, x, false);
+              x = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, x, true);
+              pb[n][w] = x;
             }
           }
-          // ---- block-scale exponents o (Sec. IV-B2)
-          int o[2];
-          o[0] = (int)fminf(fmaxf(floorf(m - tb0), 0.f), 127.f);
-          o[1] = (int)fminf(fmaxf(floorf(m - tb1), 0.f), 127.f);
-          // ---- probabilities as e4m3 codes, 32 bytes per lane per scale block
-          v8i pb[2];
-#pragma unroll
-          for (int n = 0; n < 2; ++n) {
-            if constexpr (!EXACT_P) {
-              const float cst = 8.0f * ((float)(kSigma + 7 + o[n]) - m) - kBeta;
-#pragma unroll
-              for (int w = 0; w < 8; ++w) {
-                const int u = 2 * n + (w >> 2), r0 = 4 * (w & 3);
-                uint32_t x = 0;
-                x = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sacc[u][r0 + 0], cp8, cst), 0, x);
-                x = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sacc[u][r0 + 1], cp8, cst), 1, x);
-                x = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sacc[u][r0 + 2], cp8, cst), 2, x);
-                x = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sacc[u][r0 + 3], cp8, cst), 3, x);
-                pb[n][w] = (int)x;
-              }
-            } else {
-              const float cst = (float)(kSigma + o[n]) - m;
-#pragma unroll
-              for (int w = 0; w < 8; ++w) {
-                const int u = 2 * n + (w >> 2), r0 = 4 * (w & 3);
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[u][r0 + 0], cp, cst));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[u][r0 + 1], cp, cst));
-                const float p2 = __builtin_amdgcn_exp2f(fmaf(sacc[u][r0 + 2], cp, cst));
-                const float p3 = __builtin_amdgcn_exp2f(fmaf(sacc[u][r0 + 3], cp, cst));
-                int x = 0;
-                x = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, x, false);
-                x = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, x, true);
-                pb[n][w] = x;
-              }
-            }
+        }
+        o_cur[0] = o_nxt[0];
+        o_cur[1] = o_nxt[1];
+        if constexpr (DEBUG) {
+          const int key0 = blk * kBlockKeys;
+          uint8_t* orow = a.dbg_o + ((int64_t)(b * H + h) * S + qrow) * (S / 64);
+          uint8_t* crow = a.dbg_codes + ((int64_t)(b * H + h) * S + qrow) * S;
+          if (hh == 0) {
+            orow[key0 / 64] = (uint8_t)o_cur[0];
+            orow[key0 / 64 + 1] = (uint8_t)o_cur[1];
           }
-          if constexpr (DEBUG) {
-            uint8_t* orow = a.dbg_o + ((int64_t)(b * H + h) * S + qrow) * (S / 64);
-            uint8_t* crow = a.dbg_codes + ((int64_t)(b * H + h) * S + qrow) * S;
-            if (hh == 0) {
-              orow[key0 / 64] = (uint8_t)o[0];
-              orow[key0 / 64 + 1] = (uint8_t)o[1];
-            }
-#pragma unroll
-            for (int n = 0; n < 2; ++n)
-#pragma unroll
-              for (int w = 0; w < 8; ++w) {
-                const int u = 2 * n + (w >> 2), r0 = 4 * (w & 3);
-                *(uint32_t*)(crow + key0 + 32 * u + 16 * hh + r0) = (uint32_t)pb[n][w];
-              }
-          }
-          // ---- row sum of the rounded probabilities on the matrix unit (Sec. IV-B3)
-          v4f bs[2];
 #pragma unroll
           for (int n = 0; n < 2; ++n)
-            bs[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, pb[n], zero4, 0, 0, 0, 127, 0, 127);
-          // ---- O^T += V^T P^T, the PV operand scaled by 2^-o (E8M0 code 127 - o)
 #pragma unroll
-          for (int dt = 0; dt < 4; ++dt) {
-            const int d = 32 * dt + l32;
-#pragma unroll
-            for (int n = 0; n < 2; ++n) {
-              const v4i x0 = *(const v4i*)(sv + fp8_vt_off(d, 4 * n + hh));
-              const v4i x1 = *(const v4i*)(sv + fp8_vt_off(d, 4 * n + 2 + hh));
-              oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cat8(x0, x1), pb[n], oacc[dt], 0, 0, 0,
-                                                                          127, 0, 127 - o[n]);
+            for (int w = 0; w < 8; ++w) {
+              const int u = 2 * n + (w >> 2), r0 = 4 * (w & 3);
+              *(uint32_t*)(crow + key0 + 32 * u + 16 * hh + r0) = (uint32_t)pb[n][w];
             }
-          }
-#pragma unroll
-          for (int n = 0; n < 2; ++n) l = fmaf(bs[n][0], __int_as_float((127 - o[n]) << 23), l);
         }
+      };
+      // row sums of the codes (Sec. IV-B3) and O^T += V^T P^T with the 2^-o operand scale
+      auto rowsum_pv = [&](int blk) {
+        const v8i sel = {selw, selw, selw, selw, selw, selw, selw, selw};
+        v4f bs0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, pb[0], zero4, 0, 0, 0, 127, 0, 127);
+        v4f bs1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, pb[1], zero4, 0, 0, 0, 127, 0, 127);
+        const uint8_t* sv = smem + (blk & 1) * L::kVSlot + v_rd;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int n = 0; n < 2; ++n) {
+            const v8i vop = *(const v8i*)(sv + 32 * dt * L::kVStride + 64 * n);
+            oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, pb[n], oacc[dt], 0, 0, 0, 127, 0,
+                                                                        127 - o_cur[n]);
+          }
+        return (v2f){bs0[0], bs1[0]};
+      };
 
-        if (kb + 1 < nb) store_kv(cur ^ 1);
-        __syncthreads();
+      // ---------------------------------------------------------------- prologue
+      // K(0), K(1) by group 0 threads and V(0), V(1) by group 1 threads
+      stage_load(0);
+      stage_store(0);
+      stage_load(1);
+      stage_store(1);
+      lds_barrier();
+      if (grp == 1) lds_barrier();  // group 1 runs one phase behind
+
+      // M_pro
+      if (live(0)) {
+        qk(0);
+        max_step(0, true);
       }
+      lds_barrier();
+      // S_pro
+      if (live(0)) codes(0);
+      lds_barrier();
 
-      // ---- epilogue: O = acc * dv / l in bf16, LSE in nats
+      for (int i = 0; i < nb; ++i) {
+        // -------------------------------------------------------------- M_i
+        __builtin_amdgcn_s_setprio(1);
+        const bool live_i = live(i), live_n = (i + 1 < nb) && live(i + 1);
+        if (i + 2 < nb) stage_load(i + 2);
+        if (rescale) {
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) oacc[dt] *= fres;
+          rescale = false;
+        }
+        v2f bsum = {0.f, 0.f};
+        if (live_i) bsum = rowsum_pv(i);
+        if (live_n) qk(i + 1);
+        if (live_i) l = fmaf(bsum[1], __int_as_float((127 - o_cur[1]) << 23),
+                             fmaf(bsum[0], __int_as_float((127 - o_cur[0]) << 23), l));
+        if (live_n) {
+          max_step(i + 1, false);
+          if (rescale) l *= fres;
+        }
+        lds_barrier();
+        // -------------------------------------------------------------- S_i
+        __builtin_amdgcn_s_setprio(0);
+        if (live_n) codes(i + 1);
+        if (i + 2 < nb) stage_store(i + 2);
+        lds_barrier();
+      }
+      if (grp == 0) lds_barrier();
+
+      // ---------------------------------------------------------------- epilogue
       const float inv = a.v_descale / l;
       uint16_t* op = a.out + ((int64_t)(b * S + qrow) * H + h) * 128;
 #pragma unroll
