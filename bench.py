@@ -214,6 +214,8 @@ def main():
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -225,6 +227,16 @@ def main():
     import bf16_causal_flashattention_amd as cfa
     cfa.lib()  # fail loudly when the HIP library is missing
 
+    if args.copy_calibration:
+        # a plain copy of known size: FETCH_SIZE / WRITE_SIZE of this kernel, divided by
+        # 2^30 bytes, give the scale factor of the byte counters
+        x = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(1)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 copies of 2^30 bytes")
+        del x, y
     B, H, S, D = 1, 32, 32768, 128
     head = run_fp8(torch, cfa, "fp8", synth.gaussian, B, H, S, D, args.warmup, args.steps)
     F = flops(B, H, S, D, D)

@@ -20,8 +20,8 @@
 //   group 1:  idle  M_pro S_pro M_0 S_0 ... M_{nb-1} S_{nb-1}
 // M_i: row sums of P(i); S(i+1) = K(i+1) Q^T; O += V(i)^T P(i); max of S(i+1), lazy
 //      decision, o(i+1).   S_i: P(i+1) from S(i+1).
-// Staging (global -> registers in M_i, registers -> LDS in S_i): group 0 stages K(i+2),
-// group 1 stages V(i+2)^T.  With two LDS slots per operand every write lands one phase
+// Staging (global -> registers -> LDS within S_i): group 0 stages K(i+2), group 1
+// stages V(i+2)^T.  With two LDS slots per operand every write lands one phase
 // after the slot's last read and at least one phase before its first read.
 //
 // fp32 arithmetic (the order below is part of the contract with the test oracle):
@@ -177,17 +177,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
 
       auto live = [&](int blk) { return blk * kBlockKeys <= row0 + kWaveRows - 1; };
 
-      // S^T(blk) = K(blk) Q^T into sacc
+      // S^T(blk) = K(blk) Q^T into sacc.  Chunk-outer order keeps consecutive MFMAs
+      // independent; the operand of the next MFMA is read before the current one issues.
       auto qk = [&](int blk) {
         const uint8_t* sk = smem + (blk & 1) * L::kKSlot + k_rd;
+        constexpr int N = 4 * KC;
+        v8i kop[2];
+        kop[0] = *(const v8i*)(sk);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-#pragma unroll
-          for (int c = 0; c < KC; ++c) {
-            const v8i kop = *(const v8i*)(sk + 32 * u * L::kKStride + 64 * c);
-            sacc[u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop, qop[c], c == 0 ? zero16 : sacc[u], 0,
-                                                                       0, 0, 127, 0, 127);
+        for (int t = 0; t < N; ++t) {
+          const int c = t / 4, u = t % 4;
+          if (t + 1 < N) {
+            const int c1 = (t + 1) / 4, u1 = (t + 1) % 4;
+            kop[(t + 1) & 1] = *(const v8i*)(sk + 32 * u1 * L::kKStride + 64 * c1);
           }
+          sacc[u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop[t & 1], qop[c], c == 0 ? zero16 : sacc[u], 0,
+                                                                     0, 0, 127, 0, 127);
         }
       };
       // mask, block maxima, running max with the lazy decision, exponents o for blk
@@ -280,14 +285,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
         v4f bs0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, pb[0], zero4, 0, 0, 0, 127, 0, 127);
         v4f bs1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, pb[1], zero4, 0, 0, 0, 127, 0, 127);
         const uint8_t* sv = smem + (blk & 1) * L::kVSlot + v_rd;
+        v8i vop[2];
+        vop[0] = *(const v8i*)(sv);
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-          for (int n = 0; n < 2; ++n) {
-            const v8i vop = *(const v8i*)(sv + 32 * dt * L::kVStride + 64 * n);
-            oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, pb[n], oacc[dt], 0, 0, 0, 127, 0,
-                                                                        127 - o_cur[n]);
+        for (int t = 0; t < 8; ++t) {
+          const int n = t / 4, dt = t % 4;
+          if (t + 1 < 8) {
+            const int n1 = (t + 1) / 4, dt1 = (t + 1) % 4;
+            vop[(t + 1) & 1] = *(const v8i*)(sv + 32 * dt1 * L::kVStride + 64 * n1);
           }
+          oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[t & 1], pb[n], oacc[dt], 0, 0, 0, 127, 0,
+                                                                      127 - o_cur[n]);
+        }
         return (v2f){bs0[0], bs1[0]};
       };
 
@@ -314,15 +323,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
         // -------------------------------------------------------------- M_i
         __builtin_amdgcn_s_setprio(1);
         const bool live_i = live(i), live_n = (i + 1 < nb) && live(i + 1);
-        if (i + 2 < nb) stage_load(i + 2);
         if (rescale) {
 #pragma unroll
           for (int dt = 0; dt < 4; ++dt) oacc[dt] *= fres;
           rescale = false;
         }
+        if (live_n) qk(i + 1);
         v2f bsum = {0.f, 0.f};
         if (live_i) bsum = rowsum_pv(i);
-        if (live_n) qk(i + 1);
         if (live_i) l = fmaf(bsum[1], __int_as_float((127 - o_cur[1]) << 23),
                              fmaf(bsum[0], __int_as_float((127 - o_cur[0]) << 23), l));
         if (live_n) {
@@ -332,6 +340,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
         lds_barrier();
         // -------------------------------------------------------------- S_i
         __builtin_amdgcn_s_setprio(0);
+        if (i + 2 < nb) stage_load(i + 2);  // in flight while the codes are formed
         if (live_n) codes(i + 1);
         if (i + 2 < nb) stage_store(i + 2);
         lds_barrier();
