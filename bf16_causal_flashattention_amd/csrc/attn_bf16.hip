@@ -1,13 +1,27 @@
 // Causal attention forward with BF16 operands on gfx950 MFMA (v_mfma_f32_32x32x16_bf16).
 //
 // Follows "ZYFA: Speed and Accuracy of FP8 FlashAttention on AMD CDNA4":
-//   Sec. II-B  base-2 online softmax over 128-key blocks, LSE output;
+//   Sec. II-B  base-2 online softmax over 64-key blocks, LSE output;
 //   Sec. IV-A  8 waves x 32 query rows, S^T = K Q^T so each lane holds one query's
-//              scores, causal pairing, persistent grid, chiplet map;
-//   Sec. IV-A  lazy rescaling with tau = 0.5 (the BF16 value at d = 128);
-//   Sec. VI-A  the softmax scale is applied to the fp32 scores (not folded into bf16 Q).
+//              scores, causal pairing, persistent grid, chiplet map, lazy rescaling
+//              with tau = 0.5 (the BF16 value at d = 128);
+//   Sec. VI-A  dead-block skip: in the diagonal blocks a wave skips the 64-key blocks
+//              that the causal mask hides from all its rows (loads and barriers still run);
+//   Sec. IV-D  the 8-wave ping-pong of the BF16 d = 128 kernel: the two waves of a SIMD
+//              alternate between issuing the block's matrix products and computing the
+//              softmax, with a workgroup barrier per phase;
+//   Sec. VI-A  the softmax scale multiplies the fp32 scores (not folded into bf16 Q).
+//
+// Schedule and barrier placement follow the FP8 kernel (attn_fp8.hip): group 1 (waves 4-7)
+// runs one phase behind group 0; M_i issues O += V(i)^T P(i) and S(i+1) = K(i+1) Q^T and
+// computes the next block's maximum; S_i forms P(i+1).  K and V blocks move by DMA:
+// group 0 issues K(i+2) at the end of M_i and waits at the end of S_i; group 1 issues
+// V(i+2) at the start of S_i and waits at the end of M_{i+1}.  Each lands in the slot
+// of block i, whose last read was in an earlier phase, and completes before its first
+// read.
+//
 // fp32 arithmetic: t = s * cp with cp = fp32(c log2 e); p = exp2(fmaf(s, cp, -m));
-// l sums the fp32 p; O = bf16_rne(acc / l); LSE = ln 2 * (m + log2 l).
+// l sums the fp32 p; P is p rounded to bf16; O = bf16(acc / l); LSE = ln 2 (m + log2 l).
 #include "attn_common.hpp"
 #include "attn_launch.hpp"
 
@@ -17,167 +31,225 @@ namespace {
 
 constexpr float kTauBf16 = 0.5f;
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr int kKBytes = 128 * 256;          // K block [128 keys][128 d] bf16
-constexpr int kStage = kKBytes + 128 * 256;  // + V^T block [128 d][128 keys] bf16
-constexpr int kLds = 2 * kStage;
+
+// LDS: two K slots then two V slots, each a run of 16-byte cells filled by DMA
+// (global_load_lds: lane L of a wave writes cell base + L); pad cells are never written
+// or read.
+//   K slot: row 32*(key/32) + key_perm_bf16(key%32) holds key `key` (key_perm_bf16 is an
+//           involution), 17 cells (272 bytes) per row, so lane i reads row 32u + i, which
+//           holds key 32u + key_perm_bf16(i).
+//   V slot: row r holds V[key0 + r][0..127], 18 cells (288 bytes) per row; the PV operand
+//           (V^T) comes from LDS transpose reads.
+constexpr int kBlk = 64;  // keys per block (max update, ping-pong phase and LDS slot)
+constexpr int kKSpr = 17;
+constexpr int kKStride = 16 * kKSpr;
+constexpr int kKCells = kBlk * kKSpr;
+constexpr int kKSlot = 16 * kKCells;
+constexpr int kVSpr = 18;
+constexpr int kVStride = 16 * kVSpr;
+constexpr int kVCells = kBlk * kVSpr;
+constexpr int kVSlot = 16 * kVCells;
+constexpr int kVBase = 2 * kKSlot;
+constexpr int kLdsBytes = 2 * kKSlot + 2 * kVSlot;
+constexpr int kRounds = (kVCells + 255) / 256;  // >= (kKCells + 255) / 256
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ v8bf as_bf(v4i x) { return __builtin_bit_cast(v8bf, x); }
 
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  bf2 r;
+  r[0] = (__bf16)lo;
+  r[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
+  const int grp = wave >> 2;
   const int S = a.S, H = a.H;
   const Schedule sch = make_schedule(a.B, H, S);
   const int logical = xcd_logical(blockIdx.x, gridDim.x);
+  const int rs = H * 256;  // BSHD row stride in bytes (d = 128 bf16)
 
-  const int v_dc = tid & 15, v_kg = tid >> 4;
-  const int64_t rs = (int64_t)H * 256;  // row stride in bytes (d = 128 bf16)
+  const int k_rd = l32 * kKStride + 16 * hh;
+  // V transpose-read base: 16-lane group G = lane/16, source lane s = lane%16 reads key
+  // 8hh + s/4 (+ 16mm + 4q), bf16 elements 32dt + 16 (G%2) + 4 (s%4) .. +3
+  const int v_tr = kVBase + (8 * hh + ((lane & 15) >> 2)) * kVStride + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+
+  // staging by DMA: the 256 threads of group 0 copy K blocks, those of group 1 V blocks.
+  // Round p, thread st covers cell 256p + st of the slot; st_goff is its source offset
+  // from the block's first key (-1: pad cell or past the end).
+  const int st = tid & 255;
+  const bool stage_k = (grp == 0);
+  int st_goff[kRounds];
+#pragma unroll
+  for (int p = 0; p < kRounds; ++p) {
+    const int cell = 256 * p + st;
+    if (stage_k) {
+      const int row = cell / kKSpr, col = cell % kKSpr;
+      st_goff[p] = (row < kBlk && col < 16) ? ((row & ~31) | key_perm_bf16(row & 31)) * rs + 16 * col : -1;
+    } else {
+      const int row = cell / kVSpr, col = cell % kVSpr;
+      st_goff[p] = (row < kBlk && col < 16) ? row * rs + 16 * col : -1;
+    }
+  }
+  const int st_lds = 16 * (64 * ((tid >> 6) & 3)) + (stage_k ? 0 : kVBase);
+  const v16f zero16 = {};
   const float cp = a.cp;
 
   for (int64_t item = logical; item < sch.items; item += gridDim.x) {
     int b, h, j;
     decode_item(item, H, sch.P, b, h, j);
-    const uint8_t* kbh = (const uint8_t*)a.k + ((int64_t)b * S * H + h) * 256;
-    const uint8_t* vbh = (const uint8_t*)a.v + ((int64_t)b * S * H + h) * 256;
-    const uint8_t* qbh = (const uint8_t*)a.q + ((int64_t)b * S * H + h) * 256;
+    const int64_t bh = (int64_t)b * S * H + h;
+    const uint8_t* qbh = (const uint8_t*)a.q + bh * 256;
+    const uint8_t* st_head = (const uint8_t*)(stage_k ? a.k : a.v) + bh * 256;
 
     for (int pass = 0; pass < 2; ++pass) {
       const int tile = pass == 0 ? j : sch.T - 1 - j;
       if (pass == 1 && tile == j) break;
       const int row0 = tile * kTileRows + wave * kWaveRows;
       const int qrow = row0 + l32;
-      const int nb = 2 * tile + 2;
+      const int nb = 4 * tile + 4;  // 64-key blocks
 
-      // Q^T operand: lane holds Q[qrow][16m + 8hh .. +8] for m = 0..7
-      v8bf qop[8];
+      auto stage = [&](int blk) {  // DMA of block blk into slot blk % 2
+        const uint8_t* src = st_head + (int64_t)(blk * kBlk) * rs;
+        uint8_t* dst = smem + st_lds + (blk & 1) * (stage_k ? kKSlot : kVSlot);
+#pragma unroll
+        for (int p = 0; p < kRounds; ++p)
+          if (st_goff[p] >= 0) dma16(src + st_goff[p], dst + 4096 * p);
+      };
+
+      v4i qop[8];  // Q^T operand: lane holds Q[qrow][16m + 8hh .. +8]
       {
         const uint8_t* qp = qbh + (int64_t)qrow * rs + 16 * hh;
 #pragma unroll
-        for (int m = 0; m < 8; ++m) qop[m] = as_bf(*(const v4i*)(qp + 32 * m));
+        for (int m = 0; m < 8; ++m) qop[m] = *(const v4i*)(qp + 32 * m);
       }
-
       v16f oacc[4];
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
-      float m = 0.f, l = 0.f;
+      for (int dt = 0; dt < 4; ++dt) oacc[dt] = zero16;
+      v16f sacc[2];  // scores of the next block (two 32-key sub-tiles)
+      v4i pb[4];     // P^T operand per 16-key step
+      float m = 0.f, l = 0.f, fres = 1.f;
+      bool rescale = false;
 
-      v4i kreg[4], vreg[4];
-      auto load_kv = [&](int key0) {
+      auto live = [&](int blk) { return blk * kBlk <= row0 + kWaveRows - 1; };
+      auto qk = [&](int blk) {
+        const uint8_t* sk = smem + (blk & 1) * kKSlot + k_rd;
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const int id = tid + kThreads * p;
-          kreg[p] = *(const v4i*)(kbh + (int64_t)(key0 + (id >> 4)) * rs + 16 * (id & 15));
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vreg[i] = *(const v4i*)(vbh + (int64_t)(key0 + 4 * v_kg + i) * rs + 16 * v_dc);
-      };
-      auto store_kv = [&](int stage) {
-        uint8_t* sb = smem + stage * kStage;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const int id = tid + kThreads * p;
-          *(v4i*)(sb + bf16_k_off(id >> 4, id & 15)) = kreg[p];
-        }
-        uint8_t* sv = sb + kKBytes;
-        const int grp = v_kg >> 1, within = 8 * (v_kg & 1);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t a0 = (uint32_t)vreg[0][w], a1 = (uint32_t)vreg[1][w];
-          const uint32_t a2 = (uint32_t)vreg[2][w], a3 = (uint32_t)vreg[3][w];
-          v2i even, odd;  // d = 8dc + 2w (low halves) and 8dc + 2w + 1 (high halves), keys 0..3
-          even[0] = (int)perm(a1, a0, 0x05040100u);
-          even[1] = (int)perm(a3, a2, 0x05040100u);
-          odd[0] = (int)perm(a1, a0, 0x07060302u);
-          odd[1] = (int)perm(a3, a2, 0x07060302u);
-          *(v2i*)(sv + bf16_vt_off(8 * v_dc + 2 * w, grp) + within) = even;
-          *(v2i*)(sv + bf16_vt_off(8 * v_dc + 2 * w + 1, grp) + within) = odd;
-        }
-      };
-
-      load_kv(0);
-      store_kv(0);
-      __syncthreads();
-
-      for (int kb = 0; kb < nb; ++kb) {
-        const int key0 = kb * kBlockKeys;
-        const int cur = kb & 1;
-        if (kb + 1 < nb) load_kv(key0 + kBlockKeys);
-
-        if (key0 <= row0 + kWaveRows - 1) {
-          const uint8_t* sk = smem + cur * kStage;
-          const uint8_t* sv = sk + kKBytes;
-          v16f sacc[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[u][r] = 0.f;
-            const int row = 32 * u + key_perm_bf16(l32);
-#pragma unroll
-            for (int mm = 0; mm < 8; ++mm) {
-              const v4i x = *(const v4i*)(sk + bf16_k_off(row, 2 * mm + hh));
-              sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(x), qop[mm], sacc[u], 0, 0, 0);
-            }
-          }
-          // causal mask: lane half hh, sub-tile u, register r holds key key0+32u+16(r/8)+8hh+r%8
-          if (key0 + kBlockKeys - 1 > row0) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-              for (int r = 0; r < 16; ++r)
-                if (key0 + 32 * u + 16 * (r >> 3) + 8 * hh + (r & 7) > qrow) sacc[u][r] = -INFINITY;
-          }
-          float x = -INFINITY;
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) x = fmax3(x, sacc[u][r], sacc[u][r + 1]);
-          const float tmax = max_with_partner(x) * cp;
-          if (kb == 0) {
-            m = tmax;
-          } else {
-            const float M = fmaxf(m, tmax);
-            if (__any((M - m) >= kTauBf16)) {
-              const float f = __builtin_amdgcn_exp2f(m - M);
-#pragma unroll
-              for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[dt][r] *= f;
-              l *= f;
-              m = M;
-            }
-          }
-          const float nm = -m;
-          v4i pb[8];  // P^T operand per 16-key MFMA step: 8 bf16 of sub-tile mm/2, regs 8(mm%2)..
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int mm = 0; mm < 8; ++mm) {
-            const int u = mm >> 1, r0 = 8 * (mm & 1);
-            float p[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[u][r0 + e], cp, nm));
-              l += p[e];
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) pb[mm][e] = (int)pack_bf16x2(p[2 * e], p[2 * e + 1]);
+            const v4i kop = *(const v4i*)(sk + 32 * u * kKStride + 32 * mm);
+            sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(kop), as_bf(qop[mm]), mm == 0 ? zero16 : sacc[u],
+                                                              0, 0, 0);
           }
+      };
+      // causal mask (lane half hh, sub-tile u, register r holds key key0+32u+16(r/8)+8hh+r%8),
+      // running max and the lazy decision
+      auto max_step = [&](int blk, bool first) {
+        const int key0 = blk * kBlk;
+        if (key0 + kBlk - 1 > row0) {
 #pragma unroll
-          for (int dt = 0; dt < 4; ++dt) {
-            const int d = 32 * dt + l32;
+          for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int mm = 0; mm < 8; ++mm) {
-              const v4i x = *(const v4i*)(sv + bf16_vt_off(d, 2 * mm + hh));
-              oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(x), as_bf(pb[mm]), oacc[dt], 0, 0, 0);
-            }
+            for (int r = 0; r < 16; ++r)
+              if (key0 + 32 * u + 16 * (r >> 3) + 8 * hh + (r & 7) > qrow) sacc[u][r] = -INFINITY;
+        }
+        float x = fmaxf(sacc[0][0], sacc[0][1]);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int r = (u == 0 ? 2 : 0); r < 16; r += 2) x = fmax3(x, sacc[u][r], sacc[u][r + 1]);
+        const float tmax = max_with_partner(x) * cp;
+        if (first) {
+          m = tmax;
+        } else {
+          const float M = fmaxf(m, tmax);
+          rescale = __any((M - m) >= kTauBf16);
+          if (rescale) {  // l (blocks <= blk-1) now; O after PV(blk-1) completes
+            fres = __builtin_amdgcn_exp2f(m - M);
+            l *= fres;
+            m = M;
           }
         }
+      };
+      auto probs = [&]() {
+        const float nm = -m;
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) {
+          const int u = mm >> 1, r0 = 8 * (mm & 1);
+          float p[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[u][r0 + e], cp, nm));
+          l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pb[mm][e] = (int)cvt_pk_bf16(p[2 * e], p[2 * e + 1]);
+        }
+      };
+      auto pv = [&](int blk) {
+        const uint8_t* sv = smem + (blk & 1) * kVSlot + v_tr;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int mm = 0; mm < 4; ++mm) {
+            // lane: d = 32dt + l32, bf16 of keys 16mm + 8hh + 0..7
+            const v2i r0 = lds_tr16(sv + (16 * mm) * kVStride + 64 * dt);
+            const v2i r1 = lds_tr16(sv + (16 * mm + 4) * kVStride + 64 * dt);
+            const v4i vop = {r0[0], r0[1], r1[0], r1[1]};
+            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(vop), as_bf(pb[mm]), oacc[dt], 0, 0, 0);
+          }
+      };
 
-        if (kb + 1 < nb) store_kv(cur ^ 1);
-        __syncthreads();
+      stage(0);
+      stage(1);
+      wait_dma();
+      lds_barrier();
+      if (grp == 1) lds_barrier();
+
+      if (live(0)) {
+        qk(0);
+        max_step(0, true);
       }
+      lds_barrier();
+      if (live(0)) probs();
+      lds_barrier();
+
+      for (int i = 0; i < nb; ++i) {
+        __builtin_amdgcn_s_setprio(1);
+        const bool live_i = live(i), live_n = (i + 1 < nb) && live(i + 1);
+        if (rescale) {
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) oacc[dt] *= fres;
+          rescale = false;
+        }
+        if (live_i) pv(i);
+        if (live_n) {
+          qk(i + 1);
+          max_step(i + 1, false);
+        }
+        // K(i+2) -> slot i%2 (K(i) was last read in the previous phase); group 1 waits
+        // here for the V block it issued in its previous softmax phase
+        if (stage_k && i + 2 < nb) stage(i + 2);
+        if (!stage_k && i >= 1 && i + 1 < nb) wait_dma();
+        lds_barrier();
+        __builtin_amdgcn_s_setprio(0);
+        // V(i+2) -> slot i%2 (V(i) was last read in the previous phase)
+        if (!stage_k && i + 2 < nb) stage(i + 2);
+        if (live_n) probs();
+        if (stage_k && i + 2 < nb) wait_dma();
+        lds_barrier();
+      }
+      if (grp == 0) lds_barrier();
 
       const float lt = sum_with_partner(l);
       const float inv = 1.0f / lt;
@@ -188,8 +260,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
         for (int g = 0; g < 4; ++g) {
           const int d0 = 32 * dt + 8 * g + 4 * hh;
           uint2 w;
-          w.x = pack_bf16x2(oacc[dt][4 * g + 0] * inv, oacc[dt][4 * g + 1] * inv);
-          w.y = pack_bf16x2(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
+          w.x = cvt_pk_bf16(oacc[dt][4 * g + 0] * inv, oacc[dt][4 * g + 1] * inv);
+          w.y = cvt_pk_bf16(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
           *(uint2*)(op + d0) = w;
         }
       if (a.lse != nullptr && hh == 0) a.lse[(int64_t)(b * H + h) * S + qrow] = kLn2 * (m + __log2f(lt));

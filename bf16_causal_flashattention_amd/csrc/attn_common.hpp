@@ -110,6 +110,30 @@ __device__ __forceinline__ int bf16_vt_off(int d, int grp) {
   return d * 256 + ((grp ^ f) << 4);
 }
 
+// global -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4): lane L of
+// the wave writes lds_wave_base + 16 L, whatever its source address.  Completion is
+// tracked by the issuing wave's vmcnt.
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ void dma16(const void* gsrc, uint8_t* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_void_t*)lds_wave_base, 16, 0, 0);
+}
+// s_waitcnt vmcnt(0) (gfx9 encoding: expcnt and lgkmcnt at their maxima), issued as the
+// builtin so the compiler's own wait insertion knows the counter is drained afterwards
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// LDS transpose reads (gfx950).  Within each 16-lane group of a wave:
+//   tr8:  output lane 8a+e receives byte e of the 8 bytes at the addresses of
+//         source lanes a, a+2, ..., a+14;
+//   tr16: output lane 4a+e receives element e of the 4 bf16 at the addresses of
+//         source lanes a, a+4, a+8, a+12.
+typedef short v4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v2i lds_tr8(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)p);
+}
+__device__ __forceinline__ v2i lds_tr16(const uint8_t* p) {
+  return __builtin_bit_cast(v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p));
+}
+
 // byte permute: result byte k = sel byte k indexing {lo bytes 0-3, hi bytes 4-7}
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);

@@ -194,6 +194,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
           sacc[u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop[t & 1], qop[c], c == 0 ? zero16 : sacc[u], 0,
                                                                      0, 0, 127, 0, 127);
         }
+        if constexpr (DQK == 128) {  // keep one operand read in flight ahead of each MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+          for (int t = 0; t < N - 1; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
       };
       // mask, block maxima, running max with the lazy decision, exponents o for blk
       auto max_step = [&](int blk, bool first) {
@@ -296,6 +305,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
           }
           oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[t & 1], pb[n], oacc[dt], 0, 0, 0, 127, 0,
                                                                       127 - o_cur[n]);
+        }
+        if constexpr (DQK == 128) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+          for (int t = 0; t < 7; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
         }
         return (v2f){bs0[0], bs1[0]};
       };
