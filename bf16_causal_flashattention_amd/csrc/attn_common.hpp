@@ -19,7 +19,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 // A workgroup owns a tile of 256 query rows; each of its 8 waves owns 32 rows
-// (two waves per SIMD).  Keys stream through LDS in blocks of 128.
+// (two waves per SIMD).  Keys stream through LDS in blocks of 128 (FP8) or 64 (BF16).
 constexpr int kTileRows = 256;
 constexpr int kWaves = 8;
 constexpr int kWaveRows = 32;
@@ -82,32 +82,6 @@ __host__ __device__ constexpr int key_perm_fp8(int i) {
 // 16*(r/8) + 8*hh + r%8.
 __host__ __device__ constexpr int key_perm_bf16(int i) {
   return 16 * (i >> 4) + 8 * ((i >> 2) & 1) + 4 * ((i >> 3) & 1) + (i & 3);
-}
-
-// ---------------------------------------------------------------------------
-// LDS layouts (16-byte groups XOR-swizzled so MFMA operand reads and staging
-// writes are free of bank conflicts).
-//
-// FP8 K block: d_qk/64 planes of [128 keys][64 B]; plane stride 8192+64 B.
-constexpr int kFp8KPlane = 8192 + 64;
-__device__ __forceinline__ int fp8_k_off(int plane, int row, int grp) {
-  const int f = ((row >> 1) & 1) | (((row >> 4) & 1) << 1);
-  return plane * kFp8KPlane + row * 64 + ((grp ^ f) << 4);
-}
-// FP8 V^T block: [128 d][128 keys] bytes.
-__device__ __forceinline__ int fp8_vt_off(int d, int grp) {
-  const int f = (d & 7) ^ ((d >> 3) & 7);
-  return d * 128 + ((grp ^ f) << 4);
-}
-// BF16 K block: [128 keys][256 B].
-__device__ __forceinline__ int bf16_k_off(int row, int grp) {
-  const int f = (row & 3) | (((row >> 3) & 1) << 2);
-  return row * 256 + ((grp ^ f) << 4);
-}
-// BF16 V^T block: [128 d][128 keys x 2 B].
-__device__ __forceinline__ int bf16_vt_off(int d, int grp) {
-  const int f = (d & 7) ^ ((d >> 3) & 7);
-  return d * 256 + ((grp ^ f) << 4);
 }
 
 // global -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4): lane L of
