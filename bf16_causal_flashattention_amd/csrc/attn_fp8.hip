@@ -10,19 +10,23 @@
 //                      E8M0 operand scale of the PV MFMA;
 //   Sec. IV-B3         row sum of the rounded probabilities on the matrix unit;
 //   Sec. IV-C, Fig. 6  two-wave ping-pong: the two waves of a SIMD alternate between an
-//                      MFMA phase (row sums, S^T of the next block, PV of the current
-//                      block, next block's maximum and rescale decision) and a softmax
-//                      phase (the probability codes), with a workgroup barrier per phase.
+//                      MFMA phase and a softmax phase, with a workgroup barrier per phase.
+//                      Here the softmax phase also takes the block maximum and the
+//                      rescale decision, so the MFMA wave's stream is MFMAs and operand
+//                      reads only.
 //
 // Schedule per 256-row tile with nb 128-key blocks.  Group g = wave / 4 (one wave of
 // each group per SIMD).  Group 1 runs one phase behind group 0:
 //   group 0:  M_pro S_pro M_0 S_0 M_1 S_1 ... M_{nb-1} S_{nb-1} idle
 //   group 1:  idle  M_pro S_pro M_0 S_0 ... M_{nb-1} S_{nb-1}
-// M_i: row sums of P(i); S(i+1) = K(i+1) Q^T; O += V(i)^T P(i); max of S(i+1), lazy
-//      decision, o(i+1).   S_i: P(i+1) from S(i+1).
-// Staging (global -> registers -> LDS within S_i): group 0 stages K(i+2), group 1
-// stages V(i+2)^T.  With two LDS slots per operand every write lands one phase
-// after the slot's last read and at least one phase before its first read.
+// M_i (matrix phase): row sums of P(i); S(i+1) = K(i+1) Q^T; O += V(i)^T P(i); l update.
+// S_i (softmax phase): maximum of S(i+1), lazy decision (and the rare rescale of O and
+//      l), o(i+1), P(i+1).  The matrix wave issues only MFMAs and their LDS operand reads.
+// Staging by DMA (global_load_lds, no registers): in S_i group 0 copies K(i+2) and
+// group 1 copies V(i+2) into the slot of block i, issuing at the start of the phase and
+// waiting at its end.  That slot was last read one phase earlier, and the copy completes
+// one phase before its first read; the softmax phase reads no LDS, so nothing waits on
+// the copy early.
 //
 // fp32 arithmetic (the order below is part of the contract with the test oracle):
 //   cp   = fp32(c * dq * dk * log2 e), scores s are fp32 MFMA sums
@@ -36,6 +40,7 @@
 #include "attn_common.hpp"
 #include "attn_launch.hpp"
 
+
 namespace cfa {
 
 namespace {
@@ -45,26 +50,38 @@ constexpr int kSigma = 6;          // probability shift 2^6 (Sec. IV-B1)
 constexpr float kBeta = 0.35f;     // lean-P bias (Sec. IV-B1, Eq. 2)
 constexpr float kLn2 = 0.69314718055994530942f;
 
-// LDS: two K slots then two V^T slots.
-//   K slot: row 32*(key/32) + kinv(key%32) holds key `key`, row stride DQK + 16 bytes, so
-//           lane i of a wave reads row 32u + i, which holds key 32u + key_perm_fp8(i).
-//   V^T slot: row d (128 rows, stride 144 bytes) holds V[key][d] for the block's 128 keys,
-//           16-byte key groups stored with bits 0 and 1 of the group index swapped, so a
-//           lane's 32 PV operand bytes (keys 64n+16hh+j and 64n+32+16hh+j) are contiguous.
+// LDS: two K slots then two V slots, each a run of 16-byte cells written by DMA (lane L of
+// a wave writes cell base + L).  Pad cells receive a copy of a data cell of the same row
+// (no per-lane masking) and are never read.
+//   K slot: row 32*(key/32) + kinv(key%32) holds key `key` (kKCols data cells + 1 pad cell
+//           per row), so lane i of a wave reads row 32u + i, which holds key
+//           32u + key_perm_fp8(i).
+//   V slot: row r holds V[key0 + r][0..127] (8 data cells + 2 pad cells per row).  The PV
+//           operand V^T comes from ds_read_b64_tr_b8; the 160-byte row stride keeps those
+//           reads free of bank conflicts.
 template <int DQK>
 struct Fp8Lds {
-  static constexpr int kKc = DQK / 64;
-  static constexpr int kKStride = DQK + 16;
-  static constexpr int kKSlot = 128 * kKStride;
-  static constexpr int kVStride = 144;
-  static constexpr int kVSlot = 128 * kVStride;
+  static constexpr int kKCols = DQK / 16;
+  static constexpr int kKSpr = kKCols + 1;  // cells per K row
+  static constexpr int kKStride = 16 * kKSpr;
+  static constexpr int kKCells = 128 * kKSpr;
+  static constexpr int kKSlot = 16 * kKCells;
+  static constexpr int kVSpr = 10;
+  static constexpr int kVStride = 16 * kVSpr;
+  static constexpr int kVCells = 128 * kVSpr;
+  static constexpr int kVSlot = 16 * kVCells;
   static constexpr int kVBase = 2 * kKSlot;
   static constexpr int kBytes = 2 * kKSlot + 2 * kVSlot;
-  static constexpr int kKChunksPerThread = 128 * DQK / 16 / 256;  // staged by 256 threads
+  static constexpr int kRounds = ((kKCells > kVCells ? kKCells : kVCells) + 255) / 256;  // DMA rounds, 256 threads
 };
 
-__device__ __forceinline__ int kinv(int k) { return 8 * ((k >> 2) & 3) + 4 * (k >> 4) + (k & 3); }
-__device__ __forceinline__ int vt_group(int g) { return (g & 4) | ((g & 1) << 1) | ((g >> 1) & 1); }
+// max of two floats that are never NaN, as one v_max_f32 (fmaxf would first quiet both
+// operands, which the compiler cannot prove unnecessary for MFMA and permlane results)
+__device__ __forceinline__ float max2(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -75,11 +92,12 @@ __device__ __forceinline__ void lds_barrier() {
 template <int DQK, bool EXACT_P, bool DEBUG>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
   using L = Fp8Lds<DQK>;
-  constexpr int KC = L::kKc;
+  constexpr int KC = DQK / 64;
   __shared__ __attribute__((aligned(16))) uint8_t smem[L::kBytes];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in SGPRs
+  const int lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
   const int grp = wave >> 2;  // 0: waves 0-3, 1: waves 4-7 (one of each per SIMD)
   const int S = a.S, H = a.H;
   const Schedule sch = make_schedule(a.B, H, S);
@@ -90,23 +108,34 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
 
   // per-lane LDS read bases
   const int k_rd = l32 * L::kKStride + 32 * hh;
-  const int v_rd = L::kVBase + l32 * L::kVStride + 32 * hh;
+  // V^T operand by transpose reads: within each 16-lane group, source lane s points at key
+  // (piece base) + s/2, bytes d0 + 8 (s%2) .. +7 with d0 = 32 dt + 16 ((lane/16) % 2); the
+  // reading lane then holds d = 32 dt + lane%32 for 8 consecutive keys.  The four pieces of
+  // a 64-key block n are keys 64n + 16 hh + {0, 8, 32, 40} + 0..7 (Sec. IV-A layout of P).
+  const int v_tr = L::kVBase + (16 * hh + ((lane & 15) >> 1)) * L::kVStride + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
 
-  // staging assignments: the 256 threads of group 0 stage K, those of group 1 stage V^T.
-  // Both use one register array and the same load code; only the LDS store differs.
-  constexpr int NST = L::kKChunksPerThread;  // 16-byte chunks per staging thread (>= 4)
+  // DMA assignments: the 256 threads of group 0 copy K blocks, those of group 1 V blocks.
+  // Round p, thread st covers cell 256p + st of the slot; st_goff is its source offset
+  // from the block's first key (pad cells copy column 0 of their row).  Waves whose cells
+  // of a round lie past the end of the slot skip that round (a wave-uniform test).
+  constexpr int NR = L::kRounds;
   const int st = tid & 255;
   const bool stage_k = (grp == 0);
-  const int st_rs = stage_k ? krs : vrs;  // global row stride of the staged tensor
-  int st_goff[NST], k_soff[NST];
-  const int v_kg = st & 31, v_dc = st >> 5;  // V: keys 4kg..4kg+3, d 16dc..16dc+15
+  const int wq = wave & 3;  // wave index within its group
+  const int st_cells = stage_k ? L::kKCells : L::kVCells;
+  uint32_t st_goff[NR];
 #pragma unroll
-  for (int p = 0; p < NST; ++p) {
-    const int id = st + 256 * p, key = id / (DQK / 16), gg = id % (DQK / 16);
-    st_goff[p] = stage_k ? key * krs + 16 * gg : (4 * v_kg + (p & 3)) * vrs + 16 * v_dc;
-    k_soff[p] = ((key & ~31) | kinv(key & 31)) * L::kKStride + 16 * gg;
+  for (int p = 0; p < NR; ++p) {
+    const int cell = 256 * p + st;
+    if (stage_k) {
+      const int row = (cell / L::kKSpr) & 127, col = cell % L::kKSpr;
+      st_goff[p] = ((row & ~31) | key_perm_fp8(row & 31)) * krs + 16 * (col < L::kKCols ? col : 0);
+    } else {
+      const int row = (cell / L::kVSpr) & 127, col = cell % L::kVSpr;
+      st_goff[p] = row * vrs + 16 * (col < 8 ? col : 0);
+    }
   }
-  const int v_soff = L::kVBase + 16 * v_dc * L::kVStride + 16 * vt_group(v_kg >> 2) + 4 * (v_kg & 3);
+  const int st_lds = 16 * 64 * wq + (stage_k ? 0 : L::kVBase);
 
   // row-sum selector (Sec. IV-B3): lane L of the 16x16x128 A operand is all ones
   // iff (L/16)%2 == ((L%16)/4)%2, so every lane receives the sum of its own query.
@@ -123,6 +152,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
     decode_item(item, H, sch.P, b, h, j);
     const uint8_t* qbh = a.q + ((int64_t)b * S * H + h) * DQK;
     const uint8_t* st_head = stage_k ? a.k + ((int64_t)b * S * H + h) * DQK : a.v + ((int64_t)b * S * H + h) * 128;
+    const int st_rs = stage_k ? krs : vrs;
 
     for (int pass = 0; pass < 2; ++pass) {
       const int tile = pass == 0 ? j : sch.T - 1 - j;
@@ -131,32 +161,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
       const int qrow = row0 + l32;
       const int nb = 2 * tile + 2;                             // 128-key blocks
 
-      // ---------------------------------------------------------------- staging
-      v4i stg[NST];
-      auto stage_load = [&](int blk) {  // global -> registers for block blk
-        const uint8_t* base = st_head + (int64_t)(blk * kBlockKeys) * st_rs;
+      // DMA of block blk into slot blk % 2 (K by group 0, V by group 1)
+      auto stage = [&](int blk) {
+        const uint8_t* src = st_head + (int64_t)(blk * kBlockKeys) * st_rs;
+        uint8_t* dst = smem + st_lds + (blk & 1) * (stage_k ? L::kKSlot : L::kVSlot);
 #pragma unroll
-        for (int p = 0; p < NST; ++p)
-          if (p < 4 || stage_k) stg[p] = *(const v4i*)(base + st_goff[p]);
-      };
-      auto stage_store = [&](int blk) {  // registers -> LDS slot blk % 2
-        const int slot = blk & 1;
-        if (stage_k) {
-          uint8_t* sk = smem + slot * L::kKSlot;
-#pragma unroll
-          for (int p = 0; p < NST; ++p) *(v4i*)(sk + k_soff[p]) = stg[p];
-        } else {
-          uint8_t* sv = smem + slot * L::kVSlot + v_soff;
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {  // d 16dc + 4q4 .. +3
-            uint32_t r[4], t[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) r[i] = (uint32_t)stg[i][q4];
-            transpose4x4_u8(r, t);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) *(uint32_t*)(sv + (4 * q4 + e) * L::kVStride) = t[e];
-          }
-        }
+        for (int p = 0; p < NR; ++p)
+          if (256 * p + 64 * wq < st_cells) dma16(src + st_goff[p], dst + 4096 * p);
       };
 
       // ---------------------------------------------------------------- per-wave state
@@ -171,12 +182,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
       for (int dt = 0; dt < 4; ++dt) oacc[dt] = zero16;
       v16f sacc[4];  // scores of the next block
       v8i pb[2];     // codes of the current block, per 64-key scale block
-      float m = 0.f, l = 0.f, fres = 1.f;
+      float m = 0.f, l = 0.f;
       int o_cur[2] = {0, 0}, o_nxt[2] = {0, 0};
-      bool rescale = false;
 
       auto live = [&](int blk) { return blk * kBlockKeys <= row0 + kWaveRows - 1; };
 
+      // row sums of the codes of the current block (Sec. IV-B3); register operands only, so
+      // these MFMAs start the matrix phase while the first K operand reads are in flight
+      auto rowsum = [&]() {
+        const v8i sel = {selw, selw, selw, selw, selw, selw, selw, selw};
+        const v4f bs0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, pb[0], zero4, 0, 0, 0, 127, 0, 127);
+        const v4f bs1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, pb[1], zero4, 0, 0, 0, 127, 0, 127);
+        return (v2f){bs0[0], bs1[0]};
+      };
       // S^T(blk) = K(blk) Q^T into sacc.  Chunk-outer order keeps consecutive MFMAs
       // independent; the operand of the next MFMA is read before the current one issues.
       auto qk = [&](int blk) {
@@ -204,7 +222,39 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
       };
-      // mask, block maxima, running max with the lazy decision, exponents o for blk
+      // O^T += V^T P^T with the 2^-o operand scale; V^T by transpose reads (4 per MFMA)
+      auto pv = [&](int blk) {
+        const uint8_t* sv = smem + (blk & 1) * L::kVSlot + v_tr;
+        auto vread = [&](int t) {
+          const int n = t / 4, dt = t % 4;
+          const uint8_t* p = sv + 64 * n * L::kVStride + 32 * dt;
+          const v2i r0 = lds_tr8(p);
+          const v2i r1 = lds_tr8(p + 8 * L::kVStride);
+          const v2i r2 = lds_tr8(p + 32 * L::kVStride);
+          const v2i r3 = lds_tr8(p + 40 * L::kVStride);
+          return (v8i){r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+        };
+        v8i vop[2];
+        vop[0] = vread(0);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int n = t / 4, dt = t % 4;
+          if (t + 1 < 8) vop[(t + 1) & 1] = vread(t + 1);
+          oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[t & 1], pb[n], oacc[dt], 0, 0, 0, 127, 0,
+                                                                      127 - o_cur[n]);
+        }
+        if constexpr (DQK == 128) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+#pragma unroll
+          for (int t = 0; t < 7; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        }
+      };
+      // causal mask, block maxima (v_max3 tree), running max with the lazy decision (the
+      // rare rescale of O and l happens here, in the softmax phase), exponents o for blk
       auto max_step = [&](int blk, bool first) {
         const int key0 = blk * kBlockKeys;
         if (key0 + kBlockKeys - 1 > row0) {  // diagonal block: key key0+32u+16hh+r
@@ -217,21 +267,31 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
         float bm[2];
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
-          float x = fmaxf(sacc[2 * n][0], sacc[2 * n][1]);
+          float x[11];
 #pragma unroll
-          for (int r = 2; r < 16; r += 2) x = fmax3(x, sacc[2 * n][r], sacc[2 * n][r + 1]);
+          for (int k = 0; k < 5; ++k) x[k] = fmax3(sacc[2 * n][3 * k], sacc[2 * n][3 * k + 1], sacc[2 * n][3 * k + 2]);
+          x[5] = fmax3(sacc[2 * n][15], sacc[2 * n + 1][0], sacc[2 * n + 1][1]);
 #pragma unroll
-          for (int r = 0; r < 16; r += 2) x = fmax3(x, sacc[2 * n + 1][r], sacc[2 * n + 1][r + 1]);
-          bm[n] = max_with_partner(x) * cp;
+          for (int k = 0; k < 4; ++k)
+            x[6 + k] = fmax3(sacc[2 * n + 1][2 + 3 * k], sacc[2 * n + 1][3 + 3 * k], sacc[2 * n + 1][4 + 3 * k]);
+          x[10] = max2(sacc[2 * n + 1][14], sacc[2 * n + 1][15]);
+          const float y = fmax3(fmax3(x[0], x[1], x[2]), fmax3(x[3], x[4], x[5]),
+                                fmax3(fmax3(x[6], x[7], x[8]), x[9], x[10]));
+          const uint32_t yu = __float_as_uint(y);
+          const auto sw = __builtin_amdgcn_permlane32_swap(yu, yu, false, false);
+          const float ya = __uint_as_float(sw[0]), yb = __uint_as_float(sw[1]);
+          bm[n] = max2(ya, yb) * cp;
         }
         if (first) {
           m = fmaxf(bm[0], bm[1]);
         } else {
           const float M = fmax3(m, bm[0], bm[1]);
-          rescale = __any((M - m) >= kTauFp8);
-          if (rescale) {
-            fres = __builtin_amdgcn_exp2f(m - M);
+          if (__any((M - m) >= kTauFp8)) {
+            const float f = __builtin_amdgcn_exp2f(m - M);
             m = M;
+            l *= f;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) oacc[dt] *= f;
           }
         }
 #pragma unroll
@@ -288,79 +348,45 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
             }
         }
       };
-      // row sums of the codes (Sec. IV-B3) and O^T += V^T P^T with the 2^-o operand scale
-      auto rowsum_pv = [&](int blk) {
-        const v8i sel = {selw, selw, selw, selw, selw, selw, selw, selw};
-        v4f bs0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, pb[0], zero4, 0, 0, 0, 127, 0, 127);
-        v4f bs1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, pb[1], zero4, 0, 0, 0, 127, 0, 127);
-        const uint8_t* sv = smem + (blk & 1) * L::kVSlot + v_rd;
-        v8i vop[2];
-        vop[0] = *(const v8i*)(sv);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int n = t / 4, dt = t % 4;
-          if (t + 1 < 8) {
-            const int n1 = (t + 1) / 4, dt1 = (t + 1) % 4;
-            vop[(t + 1) & 1] = *(const v8i*)(sv + 32 * dt1 * L::kVStride + 64 * n1);
-          }
-          oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[t & 1], pb[n], oacc[dt], 0, 0, 0, 127, 0,
-                                                                      127 - o_cur[n]);
-        }
-        if constexpr (DQK == 128) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
-#pragma unroll
-          for (int t = 0; t < 7; ++t) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        }
-        return (v2f){bs0[0], bs1[0]};
-      };
 
       // ---------------------------------------------------------------- prologue
-      // K(0), K(1) by group 0 threads and V(0), V(1) by group 1 threads
-      stage_load(0);
-      stage_store(0);
-      stage_load(1);
-      stage_store(1);
+      // K(0), K(1) by group 0 and V(0), V(1) by group 1
+      stage(0);
+      stage(1);
+      wait_dma();
       lds_barrier();
       if (grp == 1) lds_barrier();  // group 1 runs one phase behind
 
       // M_pro
-      if (live(0)) {
-        qk(0);
-        max_step(0, true);
-      }
+      if (live(0)) qk(0);
       lds_barrier();
       // S_pro
-      if (live(0)) codes(0);
+      if (live(0)) {
+        max_step(0, true);
+        codes(0);
+      }
       lds_barrier();
 
       for (int i = 0; i < nb; ++i) {
         // -------------------------------------------------------------- M_i
         __builtin_amdgcn_s_setprio(1);
         const bool live_i = live(i), live_n = (i + 1 < nb) && live(i + 1);
-        if (rescale) {
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) oacc[dt] *= fres;
-          rescale = false;
-        }
-        if (live_n) qk(i + 1);
         v2f bsum = {0.f, 0.f};
-        if (live_i) bsum = rowsum_pv(i);
-        if (live_i) l = fmaf(bsum[1], __int_as_float((127 - o_cur[1]) << 23),
-                             fmaf(bsum[0], __int_as_float((127 - o_cur[0]) << 23), l));
-        if (live_n) {
-          max_step(i + 1, false);
-          if (rescale) l *= fres;
+        if (live_i) bsum = rowsum();
+        if (live_n) qk(i + 1);
+        if (live_i) {
+          pv(i);
+          l = fmaf(bsum[1], __int_as_float((127 - o_cur[1]) << 23), fmaf(bsum[0], __int_as_float((127 - o_cur[0]) << 23), l));
         }
         lds_barrier();
         // -------------------------------------------------------------- S_i
         __builtin_amdgcn_s_setprio(0);
-        if (i + 2 < nb) stage_load(i + 2);  // in flight while the codes are formed
-        if (live_n) codes(i + 1);
-        if (i + 2 < nb) stage_store(i + 2);
+        if (i + 2 < nb) stage(i + 2);  // into the slot of block i, read in the previous phase
+        if (live_n) {
+          max_step(i + 1, false);
+          codes(i + 1);
+        }
+        if (i + 2 < nb) wait_dma();
         lds_barrier();
       }
       if (grp == 0) lds_barrier();
