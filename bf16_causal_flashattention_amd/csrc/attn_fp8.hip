@@ -22,11 +22,12 @@
 // M_i (matrix phase): row sums of P(i); S(i+1) = K(i+1) Q^T; O += V(i)^T P(i); l update.
 // S_i (softmax phase): maximum of S(i+1), lazy decision (and the rare rescale of O and
 //      l), o(i+1), P(i+1).  The matrix wave issues only MFMAs and their LDS operand reads.
-// Staging by DMA (global_load_lds, no registers): in S_i group 0 copies K(i+2) and
-// group 1 copies V(i+2) into the slot of block i, issuing at the start of the phase and
-// waiting at its end.  That slot was last read one phase earlier, and the copy completes
-// one phase before its first read; the softmax phase reads no LDS, so nothing waits on
-// the copy early.
+// Staging by DMA (global_load_lds, no registers): at the end of M_i, after its last
+// operand read, group 0 copies K(i+2) into the slot of K(i) (two K slots) and group 1
+// copies V(i+2) into the slot of V(i-1) (three V slots); each wave waits for its copies at
+// the end of S_i.  Every target slot was last read in an earlier phase, every copy
+// completes at least one phase before its first read, and the softmax phase reads no
+// LDS, so nothing waits on a copy early.
 //
 // fp32 arithmetic (the order below is part of the contract with the test oracle):
 //   cp   = fp32(c * dq * dk * log2 e), scores s are fp32 MFMA sums
@@ -50,8 +51,8 @@ constexpr int kSigma = 6;          // probability shift 2^6 (Sec. IV-B1)
 constexpr float kBeta = 0.35f;     // lean-P bias (Sec. IV-B1, Eq. 2)
 constexpr float kLn2 = 0.69314718055994530942f;
 
-// LDS: two K slots then two V slots, each a run of 16-byte cells written by DMA (lane L of
-// a wave writes cell base + L).  Pad cells receive a copy of a data cell of the same row
+// LDS: two K slots then three V slots, each a run of 16-byte cells written by DMA (lane L
+// of a wave writes cell base + L).  Pad cells receive a copy of a data cell of the same row
 // (no per-lane masking) and are never read.
 //   K slot: row 32*(key/32) + kinv(key%32) holds key `key` (kKCols data cells + 1 pad cell
 //           per row), so lane i of a wave reads row 32u + i, which holds key
@@ -71,7 +72,7 @@ struct Fp8Lds {
   static constexpr int kVCells = 128 * kVSpr;
   static constexpr int kVSlot = 16 * kVCells;
   static constexpr int kVBase = 2 * kKSlot;
-  static constexpr int kBytes = 2 * kKSlot + 2 * kVSlot;
+  static constexpr int kBytes = 2 * kKSlot + 3 * kVSlot;
   static constexpr int kRounds = ((kKCells > kVCells ? kKCells : kVCells) + 255) / 256;  // DMA rounds, 256 threads
 };
 
@@ -161,10 +162,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
       const int qrow = row0 + l32;
       const int nb = 2 * tile + 2;                             // 128-key blocks
 
-      // DMA of block blk into slot blk % 2 (K by group 0, V by group 1)
+      // DMA of block blk: K by group 0 into slot blk % 2, V by group 1 into slot blk % 3
       auto stage = [&](int blk) {
         const uint8_t* src = st_head + (int64_t)(blk * kBlockKeys) * st_rs;
-        uint8_t* dst = smem + st_lds + (blk & 1) * (stage_k ? L::kKSlot : L::kVSlot);
+        uint8_t* dst = smem + st_lds + (stage_k ? (blk & 1) * L::kKSlot : (blk % 3) * L::kVSlot);
 #pragma unroll
         for (int p = 0; p < NR; ++p)
           if (256 * p + 64 * wq < st_cells) dma16(src + st_goff[p], dst + 4096 * p);
@@ -224,7 +225,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
       };
       // O^T += V^T P^T with the 2^-o operand scale; V^T by transpose reads (4 per MFMA)
       auto pv = [&](int blk) {
-        const uint8_t* sv = smem + (blk & 1) * L::kVSlot + v_tr;
+        const uint8_t* sv = smem + (blk % 3) * L::kVSlot + v_tr;
         auto vread = [&](int t) {
           const int n = t / 4, dt = t % 4;
           const uint8_t* p = sv + 64 * n * L::kVStride + 32 * dt;
@@ -378,10 +379,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
           pv(i);
           l = fmaf(bsum[1], __int_as_float((127 - o_cur[1]) << 23), fmaf(bsum[0], __int_as_float((127 - o_cur[0]) << 23), l));
         }
+        // after this phase's last operand read: K(i+2) by group 0 into the slot of K(i),
+        // V(i+2) by group 1 into the slot of V(i-1); waited for at the end of S_i
+        if (i + 2 < nb) stage(i + 2);
         lds_barrier();
         // -------------------------------------------------------------- S_i
         __builtin_amdgcn_s_setprio(0);
-        if (i + 2 < nb) stage(i + 2);  // into the slot of block i, read in the previous phase
         if (live_n) {
           max_step(i + 1, false);
           codes(i + 1);
