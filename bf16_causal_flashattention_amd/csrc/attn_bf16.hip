@@ -13,12 +13,14 @@
 //   Sec. VI-A  the softmax scale multiplies the fp32 scores (not folded into bf16 Q).
 //
 // Schedule and barrier placement follow the FP8 kernel (attn_fp8.hip): group 1 (waves 4-7)
-// runs one phase behind group 0; M_i issues O += V(i)^T P(i) and S(i+1) = K(i+1) Q^T and
-// computes the next block's maximum; S_i forms P(i+1).  K and V blocks move by DMA:
-// group 0 issues K(i+2) at the end of M_i and waits at the end of S_i; group 1 issues
-// V(i+2) at the start of S_i and waits at the end of M_{i+1}.  Each lands in the slot
-// of block i, whose last read was in an earlier phase, and completes before its first
-// read.
+// runs one phase behind group 0; M_i issues O += V(i)^T P(i) and S(i+1) = K(i+1) Q^T (MFMAs
+// and their operand reads only, each operand read three MFMAs ahead, consecutive MFMAs on
+// different accumulators); S_i takes the next block's maximum, the lazy decision (with the
+// rare rescale of O and l) and forms P(i+1).  K and V blocks move by DMA issued at the end
+// of M_i, after the phase's last operand read: group 0 copies K(i+2) into the slot of
+// K(i) (two K slots), group 1 copies V(i+2) into the slot of V(i-1) (three V slots); each
+// wave waits for its copies at the end of S_i.  Every target slot was last read in an
+// earlier phase and every copy completes at least one phase before its first read.
 //
 // fp32 arithmetic: t = s * cp with cp = fp32(c log2 e); p = exp2(fmaf(s, cp, -m));
 // l sums the fp32 p; P is p rounded to bf16; O = bf16(acc / l); LSE = ln 2 (m + log2 l).
@@ -32,9 +34,9 @@ namespace {
 constexpr float kTauBf16 = 0.5f;
 constexpr float kLn2 = 0.69314718055994530942f;
 
-// LDS: two K slots then two V slots, each a run of 16-byte cells filled by DMA
-// (global_load_lds: lane L of a wave writes cell base + L); pad cells are never written
-// or read.
+// LDS: two K slots then three V slots, each a run of 16-byte cells filled by DMA
+// (global_load_lds: lane L of a wave writes cell base + L); pad cells receive a copy of a
+// data cell of the same row (no per-lane masking) and are never read.
 //   K slot: row 32*(key/32) + key_perm_bf16(key%32) holds key `key` (key_perm_bf16 is an
 //           involution), 17 cells (272 bytes) per row, so lane i reads row 32u + i, which
 //           holds key 32u + key_perm_bf16(i).
@@ -50,8 +52,16 @@ constexpr int kVStride = 16 * kVSpr;
 constexpr int kVCells = kBlk * kVSpr;
 constexpr int kVSlot = 16 * kVCells;
 constexpr int kVBase = 2 * kKSlot;
-constexpr int kLdsBytes = 2 * kKSlot + 2 * kVSlot;
+constexpr int kLdsBytes = 2 * kKSlot + 3 * kVSlot;
 constexpr int kRounds = (kVCells + 255) / 256;  // >= (kKCells + 255) / 256
+
+// max of two floats that are never NaN, as one v_max_f32 (fmaxf would first quiet both
+// operands, which the compiler cannot prove unnecessary for MFMA and permlane results)
+__device__ __forceinline__ float max2(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -73,7 +83,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in SGPRs
+  const int lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
   const int grp = wave >> 2;
   const int S = a.S, H = a.H;
   const Schedule sch = make_schedule(a.B, H, S);
@@ -87,22 +98,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
 
   // staging by DMA: the 256 threads of group 0 copy K blocks, those of group 1 V blocks.
   // Round p, thread st covers cell 256p + st of the slot; st_goff is its source offset
-  // from the block's first key (-1: pad cell or past the end).
+  // from the block's first key (pad cells copy column 0 of their row).  Waves whose cells
+  // of a round lie past the end of the slot skip that round (a wave-uniform test).
   const int st = tid & 255;
   const bool stage_k = (grp == 0);
-  int st_goff[kRounds];
+  const int wq = wave & 3;
+  const int st_cells = stage_k ? kKCells : kVCells;
+  uint32_t st_goff[kRounds];
 #pragma unroll
   for (int p = 0; p < kRounds; ++p) {
     const int cell = 256 * p + st;
     if (stage_k) {
-      const int row = cell / kKSpr, col = cell % kKSpr;
-      st_goff[p] = (row < kBlk && col < 16) ? ((row & ~31) | key_perm_bf16(row & 31)) * rs + 16 * col : -1;
+      const int row = (cell / kKSpr) & (kBlk - 1), col = cell % kKSpr;
+      st_goff[p] = ((row & ~31) | key_perm_bf16(row & 31)) * rs + 16 * (col < 16 ? col : 0);
     } else {
-      const int row = cell / kVSpr, col = cell % kVSpr;
-      st_goff[p] = (row < kBlk && col < 16) ? row * rs + 16 * col : -1;
+      const int row = (cell / kVSpr) & (kBlk - 1), col = cell % kVSpr;
+      st_goff[p] = row * rs + 16 * (col < 16 ? col : 0);
     }
   }
-  const int st_lds = 16 * (64 * ((tid >> 6) & 3)) + (stage_k ? 0 : kVBase);
+  const int st_lds = 16 * 64 * wq + (stage_k ? 0 : kVBase);
   const v16f zero16 = {};
   const float cp = a.cp;
 
@@ -122,10 +136,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
 
       auto stage = [&](int blk) {  // DMA of block blk into slot blk % 2
         const uint8_t* src = st_head + (int64_t)(blk * kBlk) * rs;
-        uint8_t* dst = smem + st_lds + (blk & 1) * (stage_k ? kKSlot : kVSlot);
+        uint8_t* dst = smem + st_lds + (stage_k ? (blk & 1) * kKSlot : (blk % 3) * kVSlot);
 #pragma unroll
         for (int p = 0; p < kRounds; ++p)
-          if (st_goff[p] >= 0) dma16(src + st_goff[p], dst + 4096 * p);
+          if (256 * p + 64 * wq < st_cells) dma16(src + st_goff[p], dst + 4096 * p);
       };
 
       v4i qop[8];  // Q^T operand: lane holds Q[qrow][16m + 8hh .. +8]
@@ -139,20 +153,32 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
       for (int dt = 0; dt < 4; ++dt) oacc[dt] = zero16;
       v16f sacc[2];  // scores of the next block (two 32-key sub-tiles)
       v4i pb[4];     // P^T operand per 16-key step
-      float m = 0.f, l = 0.f, fres = 1.f;
-      bool rescale = false;
+      float m = 0.f, l = 0.f;
 
       auto live = [&](int blk) { return blk * kBlk <= row0 + kWaveRows - 1; };
+      // S^T(blk) = K(blk) Q^T.  The two sub-tiles alternate, so consecutive MFMAs are
+      // independent, and each MFMA's operand is read one MFMA ahead.
       auto qk = [&](int blk) {
         const uint8_t* sk = smem + (blk & 1) * kKSlot + k_rd;
+        auto kread = [&](int t) { return *(const v4i*)(sk + 32 * (t & 1) * kKStride + 32 * (t >> 1)); };
+        constexpr int D = 3;  // operand reads in flight ahead of the MFMAs
+        v4i kop[D + 1];
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int t = 0; t < D; ++t) kop[t] = kread(t);
 #pragma unroll
-          for (int mm = 0; mm < 8; ++mm) {
-            const v4i kop = *(const v4i*)(sk + 32 * u * kKStride + 32 * mm);
-            sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(kop), as_bf(qop[mm]), mm == 0 ? zero16 : sacc[u],
-                                                              0, 0, 0);
-          }
+        for (int t = 0; t < 16; ++t) {
+          const int u = t & 1, mm = t >> 1;
+          if (t + D < 16) kop[(t + D) % (D + 1)] = kread(t + D);
+          sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(kop[t % (D + 1)]), as_bf(qop[mm]),
+                                                            mm == 0 ? zero16 : sacc[u], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, D, 0);
+#pragma unroll
+        for (int t = 0; t < 16 - D; ++t) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, D, 0);
       };
       // causal mask (lane half hh, sub-tile u, register r holds key key0+32u+16(r/8)+8hh+r%8),
       // running max and the lazy decision
@@ -165,21 +191,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
             for (int r = 0; r < 16; ++r)
               if (key0 + 32 * u + 16 * (r >> 3) + 8 * hh + (r & 7) > qrow) sacc[u][r] = -INFINITY;
         }
-        float x = fmaxf(sacc[0][0], sacc[0][1]);
+        // v_max3 tree over the 32 scores of the lane
+        float x[11];
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int k = 0; k < 5; ++k) x[k] = fmax3(sacc[0][3 * k], sacc[0][3 * k + 1], sacc[0][3 * k + 2]);
+        x[5] = fmax3(sacc[0][15], sacc[1][0], sacc[1][1]);
 #pragma unroll
-          for (int r = (u == 0 ? 2 : 0); r < 16; r += 2) x = fmax3(x, sacc[u][r], sacc[u][r + 1]);
-        const float tmax = max_with_partner(x) * cp;
+        for (int k = 0; k < 4; ++k) x[6 + k] = fmax3(sacc[1][2 + 3 * k], sacc[1][3 + 3 * k], sacc[1][4 + 3 * k]);
+        x[10] = max2(sacc[1][14], sacc[1][15]);
+        const float y = fmax3(fmax3(x[0], x[1], x[2]), fmax3(x[3], x[4], x[5]), fmax3(fmax3(x[6], x[7], x[8]), x[9], x[10]));
+        const uint32_t yu = __float_as_uint(y);
+        const auto sw = __builtin_amdgcn_permlane32_swap(yu, yu, false, false);
+        const float tmax = max2(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * cp;
         if (first) {
           m = tmax;
         } else {
           const float M = fmaxf(m, tmax);
-          rescale = __any((M - m) >= kTauBf16);
-          if (rescale) {  // l (blocks <= blk-1) now; O after PV(blk-1) completes
-            fres = __builtin_amdgcn_exp2f(m - M);
-            l *= fres;
+          if (__any((M - m) >= kTauBf16)) {  // O and l hold blocks <= blk-1
+            const float f = __builtin_amdgcn_exp2f(m - M);
+            l *= f;
             m = M;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) oacc[dt] *= f;
           }
         }
       };
@@ -196,18 +229,34 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
           for (int e = 0; e < 4; ++e) pb[mm][e] = (int)cvt_pk_bf16(p[2 * e], p[2 * e + 1]);
         }
       };
+      // O^T += V^T P^T.  The four d tiles alternate (independent accumulators); each
+      // MFMA's operand (two transpose reads) is read one MFMA ahead.
       auto pv = [&](int blk) {
-        const uint8_t* sv = smem + (blk & 1) * kVSlot + v_tr;
+        const uint8_t* sv = smem + (blk % 3) * kVSlot + v_tr;
+        // lane: d = 32dt + l32, bf16 of keys 16mm + 8hh + 0..7
+        auto vread = [&](int t) {
+          const int dt = t & 3, mm = t >> 2;
+          const v2i r0 = lds_tr16(sv + (16 * mm) * kVStride + 64 * dt);
+          const v2i r1 = lds_tr16(sv + (16 * mm + 4) * kVStride + 64 * dt);
+          return (v4i){r0[0], r0[1], r1[0], r1[1]};
+        };
+        constexpr int D = 3;
+        v4i vop[D + 1];
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
+        for (int t = 0; t < D; ++t) vop[t] = vread(t);
 #pragma unroll
-          for (int mm = 0; mm < 4; ++mm) {
-            // lane: d = 32dt + l32, bf16 of keys 16mm + 8hh + 0..7
-            const v2i r0 = lds_tr16(sv + (16 * mm) * kVStride + 64 * dt);
-            const v2i r1 = lds_tr16(sv + (16 * mm + 4) * kVStride + 64 * dt);
-            const v4i vop = {r0[0], r0[1], r1[0], r1[1]};
-            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(vop), as_bf(pb[mm]), oacc[dt], 0, 0, 0);
-          }
+        for (int t = 0; t < 16; ++t) {
+          const int dt = t & 3, mm = t >> 2;
+          if (t + D < 16) vop[(t + D) % (D + 1)] = vread(t + D);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(vop[t % (D + 1)]), as_bf(pb[mm]), oacc[dt], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * D, 1);
+#pragma unroll
+        for (int t = 0; t < 16 - D; ++t) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, D, 1);
       };
 
       stage(0);
@@ -216,37 +265,31 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
       lds_barrier();
       if (grp == 1) lds_barrier();
 
-      if (live(0)) {
-        qk(0);
-        max_step(0, true);
-      }
+      if (live(0)) qk(0);
       lds_barrier();
-      if (live(0)) probs();
+      if (live(0)) {
+        max_step(0, true);
+        probs();
+      }
       lds_barrier();
 
       for (int i = 0; i < nb; ++i) {
+        // -------------------------------------------------------------- M_i
         __builtin_amdgcn_s_setprio(1);
         const bool live_i = live(i), live_n = (i + 1 < nb) && live(i + 1);
-        if (rescale) {
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) oacc[dt] *= fres;
-          rescale = false;
-        }
         if (live_i) pv(i);
-        if (live_n) {
-          qk(i + 1);
-          max_step(i + 1, false);
-        }
-        // K(i+2) -> slot i%2 (K(i) was last read in the previous phase); group 1 waits
-        // here for the V block it issued in its previous softmax phase
-        if (stage_k && i + 2 < nb) stage(i + 2);
-        if (!stage_k && i >= 1 && i + 1 < nb) wait_dma();
+        if (live_n) qk(i + 1);
+        // after this phase's last operand read: K(i+2) by group 0 into the slot of K(i),
+        // V(i+2) by group 1 into the slot of V(i-1); waited for at the end of S_i
+        if (i + 2 < nb) stage(i + 2);
         lds_barrier();
+        // -------------------------------------------------------------- S_i
         __builtin_amdgcn_s_setprio(0);
-        // V(i+2) -> slot i%2 (V(i) was last read in the previous phase)
-        if (!stage_k && i + 2 < nb) stage(i + 2);
-        if (live_n) probs();
-        if (stage_k && i + 2 < nb) wait_dma();
+        if (live_n) {
+          max_step(i + 1, false);
+          probs();
+        }
+        if (i + 2 < nb) wait_dma();
         lds_barrier();
       }
       if (grp == 0) lds_barrier();
