@@ -259,7 +259,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(heads shard across GPUs with no communication; see DESIGN.md)", file=sys.stderr)
+              "(heads shard across GPUs with no communication)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -309,17 +309,19 @@ def main():
     if not args.only_headline:
         also = {}
         wb, sb = max(3, args.warmup // 4), max(5, args.steps // 4)
-        r = run_bf16(torch, cfa, 1, 32, 32768, wb, sb)
+        r = run_bf16(torch, cfa, 1, 32, 32768, wb, sb, sustained=not args.no_sustained)
         also["bf16_B1_H32_S32768_d128"] = {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4),
-                                           "pct_bf16_peak": round(100 * r["tflops"] / PEAK_TFLOPS["bf16"], 2)}
+                                           "pct_bf16_peak": round(100 * r["tflops"] / PEAK_TFLOPS["bf16"], 2),
+                                           "sustained": r.get("sustained")}
         for s in (4096, 8192, 16384):
             r = run_bf16(torch, cfa, 1, 32, s, wb, sb)
             also[f"bf16_B1_H32_S{s}_d128"] = {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4)}
             r = run_fp8(torch, cfa, "fp8", synth.gaussian, 1, 32, s, 128, wb, sb)
             also[f"fp8_B1_H32_S{s}_d128"] = {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4)}
-        r = run_fp8(torch, cfa, "mla", synth.gaussian, 1, 16, 32768, 192, wb, sb)
+        r = run_fp8(torch, cfa, "mla", synth.gaussian, 1, 16, 32768, 192, wb, sb, sustained=not args.no_sustained)
         also["mla_fp8_B1_H16_S32768_192_128"] = {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4),
-                                                  "pct_fp8_peak": round(100 * r["tflops"] / PEAK_TFLOPS["fp8"], 2)}
+                                                  "pct_fp8_peak": round(100 * r["tflops"] / PEAK_TFLOPS["fp8"], 2),
+                                                  "sustained": r.get("sustained")}
         r = run_fp8(torch, cfa, "fp8", synth.activation_like, 1, 32, 16384, 128, wb, sb)
         also["fp8_activation_like_B1_H32_S16384_d128"] = {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4)}
         result["also"] = also
