@@ -9,9 +9,13 @@ Functions mirror the C entry points:
     attn_fwd_causal_fp8(q, k, v, q_descale, k_descale, v_descale, softmax_scale=None)
     attn_fwd_causal_bf16(q, k, v, softmax_scale=None)
     attn_fwd_causal_mla(q, k, v, q_descale, k_descale, v_descale, softmax_scale=None)
+    attn_fwd_causal_fp8_ex(q, k, v, q_descale, k_descale, v_descale, softmax_scale=None, p_mode=None)
+    attn_fwd_causal_bf16_ex(q, k, v, softmax_scale=None)
     quantize_e4m3(x) -> (codes, descale)      round_bf16(x) -> bf16 tensor
 Tensors are BSHD: q, k [B, S, H, d_qk], v [B, S, H, d_v]; outputs out [B, S, H, d_v]
-(bfloat16) and lse [B, H, S] (float32).
+(bfloat16) and lse [B, H, S] (float32).  The *_ex functions take BSHD-shaped views of any
+strided layout (e.g. a BHSD tensor x passed as x.permute(0, 2, 1, 3)) with the head
+dimension contiguous, and grouped-query k/v with H_kv heads (H a multiple of H_kv).
 """
 from __future__ import annotations
 
@@ -34,6 +38,14 @@ class AttnError(RuntimeError):
         self.code = code
 
 
+P_DEFAULT, P_LEAN, P_EXACT = -1, 0, 1
+
+
+class Strides(ctypes.Structure):
+    """attn_strides: element strides (batch, head, seq) of one tensor."""
+    _fields_ = [("batch", ctypes.c_int64), ("head", ctypes.c_int64), ("seq", ctypes.c_int64)]
+
+
 _lib = None
 
 
@@ -49,6 +61,9 @@ def lib():
         L.attn_fwd_causal_mla.argtypes = [P, P, P, P, P, F, F, F, F, I, I, I, I, I, P]
         L.attn_fwd_causal_fp8_debug.argtypes = [P, P, P, P, P, F, F, F, F, I, I, I, I, I, P, P, P]
         L.attn_fwd_causal_bf16.argtypes = [P, P, P, P, P, F, I, I, I, I, I, P]
+        SP = ctypes.POINTER(Strides)
+        L.attn_fwd_causal_fp8_ex.argtypes = [P, P, P, P, P, F, F, F, F, I, I, I, I, I, I, SP, SP, SP, SP, I, P]
+        L.attn_fwd_causal_bf16_ex.argtypes = [P, P, P, P, P, F, I, I, I, I, I, I, SP, SP, SP, SP, P]
         L.attn_quantize_e4m3.argtypes = [P, I64, P, P, P, P]
         L.attn_round_bf16.argtypes = [P, I64, P, P]
         L.attn_default_grid.argtypes = [I, I, I, I]
@@ -57,7 +72,8 @@ def lib():
         L.attn_status_string.argtypes = [I]
         L.attn_status_string.restype = ctypes.c_char_p
         for name in ("attn_fwd_causal_fp8", "attn_fwd_causal_mla", "attn_fwd_causal_fp8_debug",
-                     "attn_fwd_causal_bf16", "attn_quantize_e4m3", "attn_round_bf16", "attn_default_grid"):
+                     "attn_fwd_causal_bf16", "attn_fwd_causal_fp8_ex", "attn_fwd_causal_bf16_ex",
+                     "attn_quantize_e4m3", "attn_round_bf16", "attn_default_grid"):
             getattr(L, name).restype = I
         _lib = L
     return _lib
@@ -156,6 +172,63 @@ def attn_fwd_causal_bf16(q, k, v, softmax_scale=None, out=None, lse=None):
     rc = lib().attn_fwd_causal_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), float(softmax_scale),
                                     B, H, S, dqk, dv, _stream())
     _check("attn_fwd_causal_bf16", rc)
+    return out, lse
+
+
+def _strides(t):
+    """attn_strides of a BSHD-shaped view whose head dimension is contiguous."""
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("expected a 4-D (B, S, H, d) view with a contiguous last dimension")
+    return Strides(t.stride(0), t.stride(2), t.stride(1))
+
+
+def _ex_meta(q, k, v, out, lse):
+    B, S, H, dqk = q.shape
+    Bk, Sk, Hkv, dk = k.shape
+    if (Bk, Sk, dk) != (B, S, dqk) or tuple(v.shape[:3]) != (B, S, Hkv) or Hkv == 0 or H % Hkv:
+        raise ValueError("q, k, v shapes disagree (k, v need H_kv heads with H a multiple of H_kv)")
+    dv = v.shape[3]
+    if out is None:
+        out = torch.empty((B, S, H, dv), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    if out.dtype != torch.bfloat16 or lse.dtype != torch.float32:
+        raise TypeError("out must be bfloat16 and lse float32")
+    if tuple(out.shape) != (B, S, H, dv) or tuple(lse.shape) != (B, H, S) or not lse.is_contiguous():
+        raise ValueError("out / lse shapes disagree (lse must be a dense [B, H, S] tensor)")
+    st = [_strides(t) for t in (q, k, v, out)]
+    return B, S, H, Hkv, dqk, dv, out, lse, st
+
+
+def attn_fwd_causal_fp8_ex(q, k, v, q_descale, k_descale, v_descale, softmax_scale=None, p_mode=None,
+                           out=None, lse=None):
+    """FP8 causal attention with strided BSHD-shaped views, grouped-query k/v and a P mode
+    (P_LEAN, P_EXACT or None for the default of the head dimension).  Returns (out, lse)."""
+    q, k, v = _fp8_view(q), _fp8_view(k), _fp8_view(v)
+    B, S, H, Hkv, dqk, dv, out, lse, st = _ex_meta(q, k, v, out, lse)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(dqk)
+    pm = P_DEFAULT if p_mode is None else int(p_mode)
+    rc = lib().attn_fwd_causal_fp8_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), float(q_descale),
+                                      float(k_descale), float(v_descale), float(softmax_scale), B, H, Hkv, S, dqk,
+                                      dv, *[ctypes.byref(x) for x in st], pm, _stream())
+    _check("attn_fwd_causal_fp8_ex", rc)
+    return out, lse
+
+
+def attn_fwd_causal_bf16_ex(q, k, v, softmax_scale=None, out=None, lse=None):
+    """BF16 causal attention with strided BSHD-shaped views and grouped-query k/v."""
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16:
+            raise TypeError("q, k, v must be bfloat16")
+    B, S, H, Hkv, dqk, dv, out, lse, st = _ex_meta(q, k, v, out, lse)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(dqk)
+    rc = lib().attn_fwd_causal_bf16_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), float(softmax_scale),
+                                       B, H, Hkv, S, dqk, dv, *[ctypes.byref(x) for x in st], _stream())
+    _check("attn_fwd_causal_bf16_ex", rc)
     return out, lse
 
 

@@ -17,23 +17,84 @@ int g_num_cu[kMaxDevices];  // cached compute-unit count per device (0 = unknown
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 bool good_scale(float s) { return isfinite(s) && s > 0.0f; }
 
-// common checks of the attention entry points; returns ATTN_OK or an error
-int check_attn(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int S,
-               int d_qk, int d_v, int want_qk, int want_v, int elem) {
-  if (B < 0 || H < 0 || S < 0) return ATTN_ERR_SHAPE;
-  if (d_qk != want_qk || d_v != want_v) return ATTN_ERR_SHAPE;
-  if (B == 0 || H == 0 || S == 0) return 1;  // empty problem: nothing to do
-  if (!q || !k || !v || !out) return ATTN_ERR_NULL;
-  if (S % cfa::kTileRows != 0) return ATTN_ERR_SHAPE;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return ATTN_ERR_ALIGN;
-  if (lse && !aligned(lse, 4)) return ATTN_ERR_ALIGN;
-  // every tensor must hold fewer than 2^31 elements (B, S, H < 2^31, so no overflow below)
-  const int64_t dmax = d_qk > d_v ? d_qk : d_v;
+// Problem description shared by the attention entry points (element strides).
+struct Problem {
+  const void *q, *k, *v;
+  void* out;
+  float* lse;
+  int B, H, Hkv, S, dqk, dv;
+  attn_strides sq, sk, sv, so;
+};
+
+attn_strides bshd(int S, int H, int d) {
+  attn_strides t;
+  t.batch = (int64_t)S * H * d;
+  t.head = d;
+  t.seq = (int64_t)H * d;
+  return t;
+}
+
+// one tensor: strides non-negative, byte strides multiples of 16 (16-byte rows and cells),
+// every element offset below 2^31, and 128 rows of the row stride below 2^31 bytes
+int check_tensor(const attn_strides& t, int B, int S, int heads, int d, int elem) {
+  if (t.batch < 0 || t.head < 0 || t.seq < 0) return ATTN_ERR_ARG;
+  if ((t.batch * elem) % 16 || (t.head * elem) % 16 || (t.seq * elem) % 16) return ATTN_ERR_ALIGN;
   const int64_t lim = INT64_C(1) << 31;
-  const int64_t bs = (int64_t)B * S;
-  if (bs >= lim || bs * H >= lim || bs * H * dmax >= lim) return ATTN_ERR_RANGE;
-  (void)elem;
+  if (t.batch >= lim || t.head >= lim || t.seq * elem * cfa::kBlockKeys >= lim) return ATTN_ERR_RANGE;
+  const int64_t last = (int64_t)(B - 1) * t.batch + (int64_t)(heads - 1) * t.head + (int64_t)(S - 1) * t.seq + d;
+  if (last >= lim) return ATTN_ERR_RANGE;
   return ATTN_OK;
+}
+
+// common checks of the attention entry points; returns ATTN_OK, 1 for an empty problem,
+// or an error
+int check_attn(const Problem& p, int elem) {
+  if (p.B < 0 || p.H < 0 || p.S < 0 || p.Hkv < 0) return ATTN_ERR_SHAPE;
+  if (p.B == 0 || p.H == 0 || p.S == 0) return 1;  // empty problem: nothing to do
+  if (p.Hkv < 1 || p.H % p.Hkv != 0) return ATTN_ERR_SHAPE;
+  if (!p.q || !p.k || !p.v || !p.out) return ATTN_ERR_NULL;
+  if (p.S % cfa::kTileRows != 0) return ATTN_ERR_SHAPE;
+  if (!aligned(p.q, 16) || !aligned(p.k, 16) || !aligned(p.v, 16) || !aligned(p.out, 16)) return ATTN_ERR_ALIGN;
+  if (p.lse && !aligned(p.lse, 4)) return ATTN_ERR_ALIGN;
+  const int64_t lim = INT64_C(1) << 31;
+  if ((int64_t)p.B * p.H * p.S >= lim) return ATTN_ERR_RANGE;  // lse, and the schedule's counts
+  int rc;
+  if ((rc = check_tensor(p.sq, p.B, p.S, p.H, p.dqk, elem)) != ATTN_OK) return rc;
+  if ((rc = check_tensor(p.sk, p.B, p.S, p.Hkv, p.dqk, elem)) != ATTN_OK) return rc;
+  if ((rc = check_tensor(p.sv, p.B, p.S, p.Hkv, p.dv, elem)) != ATTN_OK) return rc;
+  if ((rc = check_tensor(p.so, p.B, p.S, p.H, p.dv, 2)) != ATTN_OK) return rc;
+  return ATTN_OK;
+}
+
+cfa::TensorMap tmap(const attn_strides& t, int elem) {
+  cfa::TensorMap m;
+  m.sb = t.batch * elem;
+  m.sh = t.head * elem;
+  m.ss = (int)(t.seq * elem);
+  return m;
+}
+
+Problem make_problem(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Hkv,
+                     int S, int dqk, int dv, const attn_strides* sq, const attn_strides* sk,
+                     const attn_strides* sv, const attn_strides* so) {
+  Problem p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.lse = lse;
+  p.B = B;
+  p.H = H;
+  p.Hkv = Hkv;
+  p.S = S;
+  p.dqk = dqk;
+  p.dv = dv;
+  const int hk = Hkv > 0 ? Hkv : 1;
+  p.sq = sq ? *sq : bshd(S, H, dqk);
+  p.sk = sk ? *sk : bshd(S, hk, dqk);
+  p.sv = sv ? *sv : bshd(S, hk, dv);
+  p.so = so ? *so : bshd(S, H, dv);
+  return p;
 }
 
 int device_cu_count(int* n) {
@@ -56,35 +117,72 @@ int grid_for(int B, int H, int S, int num_cu) {
   return (int)(s.items < num_cu ? s.items : num_cu);
 }
 
-int run_fp8(const void* q, const void* k, const void* v, void* out, float* lse, float qd, float kd, float vd,
-            float sm, int B, int H, int S, int dqk, int dv, uint8_t* dbg_o, uint8_t* dbg_c, bool debug,
-            void* stream) {
-  int rc = check_attn(q, k, v, out, lse, B, H, S, dqk, dv, dqk == 192 ? 192 : 128, 128, 1);
+int run_fp8(const Problem& p, float qd, float kd, float vd, float sm, int p_mode, uint8_t* dbg_o, uint8_t* dbg_c,
+            bool debug, void* stream) {
+  if (p.dqk != 128 && p.dqk != 192) return ATTN_ERR_SHAPE;
+  if (p.dv != 128) return ATTN_ERR_SHAPE;
+  if (p_mode != ATTN_P_DEFAULT && p_mode != ATTN_P_LEAN && p_mode != ATTN_P_EXACT) return ATTN_ERR_ARG;
+  int rc = check_attn(p, 1);
   if (rc == 1) return ATTN_OK;
   if (rc != ATTN_OK) return rc;
   if (!good_scale(qd) || !good_scale(kd) || !good_scale(vd) || !good_scale(sm)) return ATTN_ERR_ARG;
   if (debug) {
     if (!dbg_o || !dbg_c) return ATTN_ERR_NULL;
-    if ((int64_t)B * H * S * S > (INT64_C(1) << 28)) return ATTN_ERR_RANGE;
+    if ((int64_t)p.B * p.H * p.S * p.S > (INT64_C(1) << 28)) return ATTN_ERR_RANGE;
   }
   const float cp = (float)((double)sm * (double)qd * (double)kd * kLog2e);
   if (!isfinite(cp) || !(cp > 0.0f)) return ATTN_ERR_ARG;
   int ncu = 0;
   if ((rc = device_cu_count(&ncu)) != ATTN_OK) return rc;
   cfa::Fp8Args a;
-  a.q = (const uint8_t*)q;
-  a.k = (const uint8_t*)k;
-  a.v = (const uint8_t*)v;
-  a.out = (uint16_t*)out;
-  a.lse = lse;
+  a.q = (const uint8_t*)p.q;
+  a.k = (const uint8_t*)p.k;
+  a.v = (const uint8_t*)p.v;
+  a.out = (uint16_t*)p.out;
+  a.lse = p.lse;
   a.cp = cp;
   a.v_descale = vd;
-  a.B = B;
-  a.H = H;
-  a.S = S;
+  a.B = p.B;
+  a.H = p.H;
+  a.S = p.S;
+  a.G = p.H / p.Hkv;
+  a.mq = tmap(p.sq, 1);
+  a.mk = tmap(p.sk, 1);
+  a.mv = tmap(p.sv, 1);
+  a.mo = tmap(p.so, 2);
   a.dbg_o = dbg_o;
   a.dbg_codes = dbg_c;
-  const hipError_t e = cfa::launch_fp8(a, dqk, debug, grid_for(B, H, S, ncu), (hipStream_t)stream);
+  const bool exact = p_mode == ATTN_P_EXACT || (p_mode == ATTN_P_DEFAULT && p.dqk == 192);
+  const hipError_t e = cfa::launch_fp8(a, p.dqk, exact, debug, grid_for(p.B, p.H, p.S, ncu), (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int run_bf16(const Problem& p, float sm, void* stream) {
+  if (p.dqk != 128 || p.dv != 128) return ATTN_ERR_SHAPE;
+  int rc = check_attn(p, 2);
+  if (rc == 1) return ATTN_OK;
+  if (rc != ATTN_OK) return rc;
+  if (!good_scale(sm)) return ATTN_ERR_ARG;
+  const float cp = (float)((double)sm * kLog2e);
+  if (!isfinite(cp) || !(cp > 0.0f)) return ATTN_ERR_ARG;
+  int ncu = 0;
+  if ((rc = device_cu_count(&ncu)) != ATTN_OK) return rc;
+  cfa::Bf16Args a;
+  a.q = (const uint16_t*)p.q;
+  a.k = (const uint16_t*)p.k;
+  a.v = (const uint16_t*)p.v;
+  a.out = (uint16_t*)p.out;
+  a.lse = p.lse;
+  a.cp = cp;
+  a.B = p.B;
+  a.H = p.H;
+  a.S = p.S;
+  a.G = p.H / p.Hkv;
+  a.mq = tmap(p.sq, 2);
+  a.mk = tmap(p.sk, 2);
+  a.mv = tmap(p.sv, 2);
+  a.mo = tmap(p.so, 2);
+  const hipError_t e = cfa::launch_bf16(a, grid_for(p.B, p.H, p.S, ncu), (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -96,49 +194,50 @@ int attn_fwd_causal_fp8(const void* q, const void* k, const void* v, void* out, 
                         float k_descale, float v_descale, float softmax_scale, int B, int H, int S, int d_qk,
                         int d_v, void* stream) {
   if (d_qk != 128) return ATTN_ERR_SHAPE;
-  return run_fp8(q, k, v, out, lse, q_descale, k_descale, v_descale, softmax_scale, B, H, S, d_qk, d_v, nullptr,
-                 nullptr, false, stream);
+  const Problem p = make_problem(q, k, v, out, lse, B, H, H, S, d_qk, d_v, nullptr, nullptr, nullptr, nullptr);
+  return run_fp8(p, q_descale, k_descale, v_descale, softmax_scale, ATTN_P_LEAN, nullptr, nullptr, false, stream);
 }
 
 int attn_fwd_causal_mla(const void* q, const void* k, const void* v, void* out, float* lse, float q_descale,
                         float k_descale, float v_descale, float softmax_scale, int B, int H, int S, int d_qk,
                         int d_v, void* stream) {
   if (d_qk != 192) return ATTN_ERR_SHAPE;
-  return run_fp8(q, k, v, out, lse, q_descale, k_descale, v_descale, softmax_scale, B, H, S, d_qk, d_v, nullptr,
-                 nullptr, false, stream);
+  const Problem p = make_problem(q, k, v, out, lse, B, H, H, S, d_qk, d_v, nullptr, nullptr, nullptr, nullptr);
+  return run_fp8(p, q_descale, k_descale, v_descale, softmax_scale, ATTN_P_EXACT, nullptr, nullptr, false, stream);
+}
+
+int attn_fwd_causal_fp8_ex(const void* q, const void* k, const void* v, void* out, float* lse, float q_descale,
+                           float k_descale, float v_descale, float softmax_scale, int B, int H, int H_kv, int S,
+                           int d_qk, int d_v, const attn_strides* q_strides, const attn_strides* k_strides,
+                           const attn_strides* v_strides, const attn_strides* out_strides, int p_mode,
+                           void* stream) {
+  const Problem p = make_problem(q, k, v, out, lse, B, H, H_kv, S, d_qk, d_v, q_strides, k_strides, v_strides,
+                                 out_strides);
+  return run_fp8(p, q_descale, k_descale, v_descale, softmax_scale, p_mode, nullptr, nullptr, false, stream);
 }
 
 int attn_fwd_causal_fp8_debug(const void* q, const void* k, const void* v, void* out, float* lse,
                               float q_descale, float k_descale, float v_descale, float softmax_scale, int B,
                               int H, int S, int d_qk, int d_v, uint8_t* dbg_o, uint8_t* dbg_codes,
                               void* stream) {
-  if (d_qk != 128 && d_qk != 192) return ATTN_ERR_SHAPE;
-  return run_fp8(q, k, v, out, lse, q_descale, k_descale, v_descale, softmax_scale, B, H, S, d_qk, d_v, dbg_o,
-                 dbg_codes, true, stream);
+  const Problem p = make_problem(q, k, v, out, lse, B, H, H, S, d_qk, d_v, nullptr, nullptr, nullptr, nullptr);
+  return run_fp8(p, q_descale, k_descale, v_descale, softmax_scale, ATTN_P_DEFAULT, dbg_o, dbg_codes, true,
+                 stream);
 }
 
 int attn_fwd_causal_bf16(const void* q, const void* k, const void* v, void* out, float* lse,
                          float softmax_scale, int B, int H, int S, int d_qk, int d_v, void* stream) {
-  int rc = check_attn(q, k, v, out, lse, B, H, S, d_qk, d_v, 128, 128, 2);
-  if (rc == 1) return ATTN_OK;
-  if (rc != ATTN_OK) return rc;
-  if (!good_scale(softmax_scale)) return ATTN_ERR_ARG;
-  const float cp = (float)((double)softmax_scale * kLog2e);
-  if (!isfinite(cp) || !(cp > 0.0f)) return ATTN_ERR_ARG;
-  int ncu = 0;
-  if ((rc = device_cu_count(&ncu)) != ATTN_OK) return rc;
-  cfa::Bf16Args a;
-  a.q = (const uint16_t*)q;
-  a.k = (const uint16_t*)k;
-  a.v = (const uint16_t*)v;
-  a.out = (uint16_t*)out;
-  a.lse = lse;
-  a.cp = cp;
-  a.B = B;
-  a.H = H;
-  a.S = S;
-  const hipError_t e = cfa::launch_bf16(a, grid_for(B, H, S, ncu), (hipStream_t)stream);
-  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+  const Problem p = make_problem(q, k, v, out, lse, B, H, H, S, d_qk, d_v, nullptr, nullptr, nullptr, nullptr);
+  return run_bf16(p, softmax_scale, stream);
+}
+
+int attn_fwd_causal_bf16_ex(const void* q, const void* k, const void* v, void* out, float* lse,
+                            float softmax_scale, int B, int H, int H_kv, int S, int d_qk, int d_v,
+                            const attn_strides* q_strides, const attn_strides* k_strides,
+                            const attn_strides* v_strides, const attn_strides* out_strides, void* stream) {
+  const Problem p = make_problem(q, k, v, out, lse, B, H, H_kv, S, d_qk, d_v, q_strides, k_strides, v_strides,
+                                 out_strides);
+  return run_bf16(p, softmax_scale, stream);
 }
 
 int attn_quantize_e4m3(const float* x, int64_t n, uint8_t* codes, float* descale, uint32_t* workspace,

@@ -89,7 +89,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
   const int S = a.S, H = a.H;
   const Schedule sch = make_schedule(a.B, H, S);
   const int logical = xcd_logical(blockIdx.x, gridDim.x);
-  const int rs = H * 256;  // BSHD row stride in bytes (d = 128 bf16)
+  const int krs = a.mk.ss, vrs = a.mv.ss;  // key / value row strides in bytes
 
   const int k_rd = l32 * kKStride + 16 * hh;
   // V transpose-read base: 16-lane group G = lane/16, source lane s = lane%16 reads key
@@ -110,10 +110,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
     const int cell = 256 * p + st;
     if (stage_k) {
       const int row = (cell / kKSpr) & (kBlk - 1), col = cell % kKSpr;
-      st_goff[p] = ((row & ~31) | key_perm_bf16(row & 31)) * rs + 16 * (col < 16 ? col : 0);
+      st_goff[p] = ((row & ~31) | key_perm_bf16(row & 31)) * krs + 16 * (col < 16 ? col : 0);
     } else {
       const int row = (cell / kVSpr) & (kBlk - 1), col = cell % kVSpr;
-      st_goff[p] = row * rs + 16 * (col < 16 ? col : 0);
+      st_goff[p] = row * vrs + 16 * (col < 16 ? col : 0);
     }
   }
   const int st_lds = 16 * 64 * wq + (stage_k ? 0 : kVBase);
@@ -123,9 +123,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
   for (int64_t item = logical; item < sch.items; item += gridDim.x) {
     int b, h, j;
     decode_item(item, H, sch.P, b, h, j);
-    const int64_t bh = (int64_t)b * S * H + h;
-    const uint8_t* qbh = (const uint8_t*)a.q + bh * 256;
-    const uint8_t* st_head = (const uint8_t*)(stage_k ? a.k : a.v) + bh * 256;
+    const int hk = h / a.G;  // key/value head of query head h
+    const uint8_t* qbh = (const uint8_t*)a.q + b * a.mq.sb + h * a.mq.sh;
+    const uint8_t* st_head = stage_k ? (const uint8_t*)a.k + b * a.mk.sb + hk * a.mk.sh
+                                     : (const uint8_t*)a.v + b * a.mv.sb + hk * a.mv.sh;
+    const int st_rs = stage_k ? krs : vrs;
 
     for (int pass = 0; pass < 2; ++pass) {
       const int tile = pass == 0 ? j : sch.T - 1 - j;
@@ -134,8 +136,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
       const int qrow = row0 + l32;
       const int nb = 4 * tile + 4;  // 64-key blocks
 
-      auto stage = [&](int blk) {  // DMA of block blk into slot blk % 2
-        const uint8_t* src = st_head + (int64_t)(blk * kBlk) * rs;
+      auto stage = [&](int blk) {  // DMA of block blk: K into slot blk % 2, V into slot blk % 3
+        const uint8_t* src = st_head + (int64_t)(blk * kBlk) * st_rs;
         uint8_t* dst = smem + st_lds + (stage_k ? (blk & 1) * kKSlot : (blk % 3) * kVSlot);
 #pragma unroll
         for (int p = 0; p < kRounds; ++p)
@@ -144,7 +146,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
 
       v4i qop[8];  // Q^T operand: lane holds Q[qrow][16m + 8hh .. +8]
       {
-        const uint8_t* qp = qbh + (int64_t)qrow * rs + 16 * hh;
+        const uint8_t* qp = qbh + (int64_t)qrow * a.mq.ss + 16 * hh;
 #pragma unroll
         for (int m = 0; m < 8; ++m) qop[m] = *(const v4i*)(qp + 32 * m);
       }
@@ -296,7 +298,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
 
       const float lt = sum_with_partner(l);
       const float inv = 1.0f / lt;
-      uint16_t* op = a.out + ((int64_t)(b * S + qrow) * H + h) * 128;
+      uint16_t* op = (uint16_t*)((uint8_t*)a.out + b * a.mo.sb + h * a.mo.sh + (int64_t)qrow * a.mo.ss);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll

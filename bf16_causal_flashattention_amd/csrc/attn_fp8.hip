@@ -104,8 +104,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
   const Schedule sch = make_schedule(a.B, H, S);
   const int logical = xcd_logical(blockIdx.x, gridDim.x);
 
-  const int krs = H * DQK;  // BSHD key row stride in bytes (tensor < 2^31 elements)
-  const int vrs = H * 128;
+  const int krs = a.mk.ss, vrs = a.mv.ss;  // key / value row strides in bytes
 
   // per-lane LDS read bases
   const int k_rd = l32 * L::kKStride + 32 * hh;
@@ -151,8 +150,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
   for (int64_t item = logical; item < sch.items; item += gridDim.x) {
     int b, h, j;
     decode_item(item, H, sch.P, b, h, j);
-    const uint8_t* qbh = a.q + ((int64_t)b * S * H + h) * DQK;
-    const uint8_t* st_head = stage_k ? a.k + ((int64_t)b * S * H + h) * DQK : a.v + ((int64_t)b * S * H + h) * 128;
+    const int hk = h / a.G;  // key/value head of query head h
+    const uint8_t* qbh = a.q + b * a.mq.sb + h * a.mq.sh;
+    const uint8_t* st_head = stage_k ? a.k + b * a.mk.sb + hk * a.mk.sh : a.v + b * a.mv.sb + hk * a.mv.sh;
     const int st_rs = stage_k ? krs : vrs;
 
     for (int pass = 0; pass < 2; ++pass) {
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
       // ---------------------------------------------------------------- per-wave state
       v8i qop[KC];
       {
-        const uint8_t* qp = qbh + (int64_t)qrow * krs + 32 * hh;
+        const uint8_t* qp = qbh + (int64_t)qrow * a.mq.ss + 32 * hh;
 #pragma unroll
         for (int c = 0; c < KC; ++c) qop[c] = *(const v8i*)(qp + 64 * c);
       }
@@ -396,7 +396,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
 
       // ---------------------------------------------------------------- epilogue
       const float inv = a.v_descale / l;
-      uint16_t* op = a.out + ((int64_t)(b * S + qrow) * H + h) * 128;
+      uint16_t* op = (uint16_t*)((uint8_t*)a.out + b * a.mo.sb + h * a.mo.sh + (int64_t)qrow * a.mo.ss);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -415,17 +415,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
 
 }  // namespace
 
-hipError_t launch_fp8(const Fp8Args& a, int dqk, bool debug, int grid, hipStream_t stream) {
-  if (dqk == 128) {
-    if (debug)
-      hipLaunchKernelGGL((attn_fwd_fp8_kernel<128, false, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+hipError_t launch_fp8(const Fp8Args& a, int dqk, bool exact_p, bool debug, int grid, hipStream_t stream) {
+  const dim3 g(grid), t(kThreads);
+  if (debug) {  // the test hook runs the default P mode of each head dimension
+    if (dqk == 128)
+      hipLaunchKernelGGL((attn_fwd_fp8_kernel<128, false, true>), g, t, 0, stream, a);
     else
-      hipLaunchKernelGGL((attn_fwd_fp8_kernel<128, false, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((attn_fwd_fp8_kernel<192, true, true>), g, t, 0, stream, a);
+  } else if (dqk == 128) {
+    if (exact_p)
+      hipLaunchKernelGGL((attn_fwd_fp8_kernel<128, true, false>), g, t, 0, stream, a);
+    else
+      hipLaunchKernelGGL((attn_fwd_fp8_kernel<128, false, false>), g, t, 0, stream, a);
   } else {
-    if (debug)
-      hipLaunchKernelGGL((attn_fwd_fp8_kernel<192, true, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+    if (exact_p)
+      hipLaunchKernelGGL((attn_fwd_fp8_kernel<192, true, false>), g, t, 0, stream, a);
     else
-      hipLaunchKernelGGL((attn_fwd_fp8_kernel<192, true, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((attn_fwd_fp8_kernel<192, false, false>), g, t, 0, stream, a);
   }
   return hipGetLastError();
 }

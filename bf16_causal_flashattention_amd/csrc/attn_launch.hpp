@@ -5,30 +5,42 @@
 
 namespace cfa {
 
+// Byte strides of one attention tensor: element (b, s, h, d) of it sits at
+// base + b * sb + h * sh + s * ss + d * (element size); the head dimension is contiguous.
+struct TensorMap {
+  int64_t sb;  // batch stride
+  int64_t sh;  // head stride
+  int ss;      // sequence (row) stride; 128 rows of it fit in 31 bits
+};
+
 struct Fp8Args {
-  const uint8_t* q;  // e4m3 codes, BSHD [B][S][H][d_qk]
-  const uint8_t* k;  // e4m3 codes, BSHD [B][S][H][d_qk]
-  const uint8_t* v;  // e4m3 codes, BSHD [B][S][H][128]
-  uint16_t* out;     // bf16 bits, BSHD [B][S][H][128]
-  float* lse;        // [B][H][S] or null
+  const uint8_t* q;  // e4m3 codes, [B][S][H][d_qk] through mq
+  const uint8_t* k;  // e4m3 codes, [B][S][H_kv][d_qk] through mk
+  const uint8_t* v;  // e4m3 codes, [B][S][H_kv][128] through mv
+  uint16_t* out;     // bf16 bits, [B][S][H][128] through mo
+  float* lse;        // [B][H][S] (contiguous) or null
   float cp;          // fp32(softmax_scale * q_descale * k_descale * log2 e)
   float v_descale;
   int B, H, S;
+  int G;             // query heads per key/value head (H / H_kv): head h reads key/value head h / G
+  TensorMap mq, mk, mv, mo;
   uint8_t* dbg_o;      // debug build only: [B*H*S][S/64] block exponents
   uint8_t* dbg_codes;  // debug build only: [B*H*S][S] probability codes
 };
 
 struct Bf16Args {
-  const uint16_t* q;  // bf16 bits, BSHD [B][S][H][128]
-  const uint16_t* k;
-  const uint16_t* v;
-  uint16_t* out;
+  const uint16_t* q;  // bf16 bits, [B][S][H][128] through mq
+  const uint16_t* k;  // [B][S][H_kv][128] through mk
+  const uint16_t* v;  // [B][S][H_kv][128] through mv
+  uint16_t* out;      // [B][S][H][128] through mo
   float* lse;
   float cp;  // fp32(softmax_scale * log2 e)
   int B, H, S;
+  int G;
+  TensorMap mq, mk, mv, mo;
 };
 
-hipError_t launch_fp8(const Fp8Args& a, int dqk, bool debug, int grid, hipStream_t stream);
+hipError_t launch_fp8(const Fp8Args& a, int dqk, bool exact_p, bool debug, int grid, hipStream_t stream);
 hipError_t launch_bf16(const Bf16Args& a, int grid, hipStream_t stream);
 hipError_t launch_quantize_e4m3(const float* x, int64_t n, uint8_t* codes, float* descale, uint32_t* ws,
                                 hipStream_t stream);

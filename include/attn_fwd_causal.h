@@ -11,10 +11,12 @@
  * multi-head attention, BF16 or e4m3 operands with one fp32 scale per tensor,
  * BF16 output and fp32 LSE.
  *
- * Layout (all tensors dense, row-major):
+ * Layout of the basic entry points (all tensors dense, row-major):
  *   q, k : [B][S][H][d_qk]   (BSHD, the (batch, seqlen, heads, headdim) order)
  *   v    : [B][S][H][d_v]
  *   out  : [B][S][H][d_v]    bf16
+ * The *_ex entry points take any strided layout (BSHD, BHSD, ...) and grouped-query
+ * attention (H query heads over H_kv key/value heads; Table VI lists both).
  *   lse  : [B][H][S]         fp32, natural log of sum_j exp(c q_i.k_j) over visible
  *                            keys (for FP8, of the rounded probabilities; Sec. IV-B3)
  * e4m3 is the OCP "fn" variant (bias 7, max 448, no infinities), not FNUZ.
@@ -53,6 +55,22 @@ typedef enum {
   ATTN_ERR_DEVICE = -7  /* no usable device / device query failed */
 } attn_status;
 
+/* Element strides of one attention tensor for the *_ex entry points: element
+ * (b, s, h, d) sits at base + b*batch + h*head + s*seq + d (the head dimension is
+ * contiguous).  BSHD [B][S][H][D] is {S*H*D, D, H*D}; BHSD [B][H][S][D] is {H*S*D, S*D, D}.
+ * Every stride must be >= 0 and a multiple of 16 bytes, every element offset below 2^31,
+ * and 128 rows of the seq stride below 2^31 bytes; tensors must not overlap `out`. */
+typedef struct {
+  int64_t batch;
+  int64_t head;
+  int64_t seq;
+} attn_strides;
+
+/* FP8 probability mode (paper Sec. IV-B1): lean P forms each e4m3 code with one
+ * multiply-add and an integer conversion; exact P rounds 2^x to e4m3.  DEFAULT is the
+ * paper's choice per shape: lean P at d_qk = 128, exact P at d_qk = 192. */
+enum { ATTN_P_DEFAULT = -1, ATTN_P_LEAN = 0, ATTN_P_EXACT = 1 };
+
 /* FP8 causal attention at head dimension 128 with lean P.
  * Paper Sec. IV-B1 (Eq. 2: each probability's e4m3 code from one multiply-add and
  * an integer conversion), Sec. IV-B2 (per-64-key-block power-of-two scaling undone
@@ -80,6 +98,27 @@ int attn_fwd_causal_mla(const void* q, const void* k, const void* v, void* out, 
                         float k_descale, float v_descale, float softmax_scale, int B, int H, int S, int d_qk,
                         int d_v, void* stream);
 
+/* General FP8 entry point: d_qk in {128, 192}, d_v = 128, H query heads and H_kv
+ * key/value heads (H a multiple of H_kv; query head h reads key/value head
+ * h / (H / H_kv), the grouped-query attention of paper Table VI), per-tensor strides
+ * (NULL = dense BSHD with H heads for q/out and H_kv heads for k/v), and the P mode
+ * (ATTN_P_*).  lse stays dense [B][H][S].  Other arguments and errors as for
+ * attn_fwd_causal_fp8; ATTN_ERR_ARG for an unknown p_mode or a negative stride,
+ * ATTN_ERR_ALIGN for a stride that is not a multiple of 16 bytes, ATTN_ERR_SHAPE when
+ * H_kv does not divide H. */
+int attn_fwd_causal_fp8_ex(const void* q, const void* k, const void* v, void* out, float* lse, float q_descale,
+                           float k_descale, float v_descale, float softmax_scale, int B, int H, int H_kv, int S,
+                           int d_qk, int d_v, const attn_strides* q_strides, const attn_strides* k_strides,
+                           const attn_strides* v_strides, const attn_strides* out_strides, int p_mode,
+                           void* stream);
+
+/* General BF16 entry point: d_qk = d_v = 128 with grouped-query heads and strides as for
+ * attn_fwd_causal_fp8_ex (strides in bf16 elements). */
+int attn_fwd_causal_bf16_ex(const void* q, const void* k, const void* v, void* out, float* lse,
+                            float softmax_scale, int B, int H, int H_kv, int S, int d_qk, int d_v,
+                            const attn_strides* q_strides, const attn_strides* k_strides,
+                            const attn_strides* v_strides, const attn_strides* out_strides, void* stream);
+
 /* Per-tensor power-of-two e4m3 quantiser (paper Sec. V-E, footnote 17): finds
  * amax = max |x|, takes the largest 2^k with amax * 2^k <= 448 (k clamped to
  * [-126, 126], k = 0 when amax = 0), writes codes[i] = e4m3_rne(x[i] * 2^k) and
@@ -93,7 +132,8 @@ int attn_quantize_e4m3(const float* x, int64_t n, uint8_t* codes, float* descale
  * error measurement are the inputs rounded to BF16).  out: n uint16 bit patterns. */
 int attn_round_bf16(const float* x, int64_t n, uint16_t* out, void* stream);
 
-/* Test hooks.  Same computation as attn_fwd_causal_fp8 / attn_fwd_causal_mla, and
+/* Test hooks.  Same computation as attn_fwd_causal_fp8 / attn_fwd_causal_mla (dense
+ * BSHD, H_kv = H, the default P mode of the head dimension), and
  * in addition the kernel writes, for every (b, h, query row) and every block it
  * processes, the block-scale exponent o of each 64-key block (dbg_o, [B*H*S][S/64]
  * bytes) and the e4m3 code of every probability it forms (dbg_codes, [B*H*S][S]

@@ -84,6 +84,59 @@ def test_validation_errors_descales(call):
     assert call(vd=float("nan")) == -5
 
 
+def _st(b, h, s):
+    return ctypes.byref(cfa.Strides(b, h, s))
+
+
+def _fp8_ex(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, qd=1.0, kd=1.0, vd=1.0, sm=0.1, B=1, H=4, Hkv=2, S=256,
+             dqk=128, dv=128, sq=None, sk=None, sv=None, so=None, pm=-1)
+    a.update(kw)
+    return cfa.lib().attn_fwd_causal_fp8_ex(a["q"], a["k"], a["v"], a["out"], a["lse"], a["qd"], a["kd"], a["vd"],
+                                            a["sm"], a["B"], a["H"], a["Hkv"], a["S"], a["dqk"], a["dv"], a["sq"],
+                                            a["sk"], a["sv"], a["so"], a["pm"], None)
+
+
+def _bf16_ex(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, sm=0.1, B=1, H=4, Hkv=2, S=256, dqk=128, dv=128,
+             sq=None, sk=None, sv=None, so=None)
+    a.update(kw)
+    return cfa.lib().attn_fwd_causal_bf16_ex(a["q"], a["k"], a["v"], a["out"], a["lse"], a["sm"], a["B"], a["H"],
+                                             a["Hkv"], a["S"], a["dqk"], a["dv"], a["sq"], a["sk"], a["sv"],
+                                             a["so"], None)
+
+
+@pytest.mark.parametrize("call", [_fp8_ex, _bf16_ex])
+def test_ex_validation_errors(call):
+    assert call(q=None) == -1
+    assert call(Hkv=3) == -2             # H_kv must divide H
+    assert call(Hkv=0) == -2
+    assert call(Hkv=-1) == -2
+    assert call(S=384) == -2
+    assert call(dv=64) == -2
+    assert call(sq=_st(-1, 128, 512)) == -5                  # negative stride
+    assert call(sk=_st(65536, 130, 256)) == -3               # head stride not 16-byte aligned
+    assert call(so=_st(1 << 31, 128, 512)) == -4             # batch stride beyond 2^31
+    assert call(sv=_st(1 << 20, 1 << 27, 1 << 24)) == -4     # 128 rows of the seq stride beyond 2^31 bytes
+    assert call(B=0, q=None, k=None, v=None, out=None) == 0  # empty problem
+    assert call(sm=0.0) == -5
+
+
+def test_ex_p_mode_and_head_dims():
+    assert _fp8_ex(pm=2) == -5
+    assert _fp8_ex(pm=-2) == -5
+    assert _fp8_ex(dqk=192, pm=5) == -5
+    assert _fp8_ex(dqk=64) == -2
+    assert _bf16_ex(dqk=192) == -2
+
+
+def test_ex_bhsd_extent_checked():
+    # BHSD strides whose last element offset reaches 2^31 are rejected before any launch
+    B, H, S, D = 2, 64, 1 << 17, 128   # 2^31 elements in total
+    bhsd = _st(H * S * D, S * D, D)
+    assert _fp8_ex(B=B, H=H, Hkv=H, S=S, sq=bhsd) == -4
+
+
 def test_head_dims_per_entry_point():
     assert _fp8(dqk=192) == -2
     assert _mla(dqk=128) == -2

@@ -1,0 +1,152 @@
+"""GPU parity of the general entry points: grouped-query attention (H query heads over
+H_kv key/value heads, paper Table VI), strided layouts (BHSD, BSHD with padded heads),
+and the FP8 probability mode at both head dimensions (lean P at d_qk = 192 and exact P
+at 128, paper Sec. IV-B1 and the MLA ablation of Sec. VI-A).
+
+Two kinds of check per case:
+  * against the oracle, with k/v expanded to H heads on the host (query head h reads
+    key/value head h // (H / H_kv)) and the tensors brought back to dense BSHD;
+  * bit for bit against the basic BSHD entry point run on dense copies with the key/value
+    heads expanded: only the addressing differs, so the outputs must be identical.
+Each test prints its case before touching the GPU."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import bf16_causal_flashattention_amd as cfa
+import oracle
+import synth
+from gpu_util import (DEV, LSE_EMU_NATS, LSE_FP64_NATS, TOL_EMU_MAXABS, TOL_EMU_RMS, TOL_FP64_RMS_BF16,
+                      TOL_FP64_RMS_FP8, all_groups, gpu_rows, lse_rows, rms_rel)
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(*a):
+    print("CASE", *a, flush=True)
+
+
+def _relayout(x, layout):
+    """A BSHD-shaped view of a copy of x (dense BSHD GPU tensor) stored in `layout`."""
+    if layout == "bshd":
+        return x.clone()
+    if layout == "bhsd":
+        return x.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    if layout == "padded":  # BSHD with two spare heads per row
+        B, S, H, d = x.shape
+        buf = torch.zeros((B, S, H + 2, d), dtype=x.dtype, device=x.device)
+        buf[:, :, 1:H + 1] = x
+        return buf[:, :, 1:H + 1]
+    raise ValueError(layout)
+
+
+def _out_like(B, S, H, layout):
+    o = torch.full((B, S, H, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+    return _relayout(o, layout)
+
+
+def _inputs(B, H, Hkv, S, dqk, seed):
+    q = synth.gaussian(B, S, H, dqk, 128, seed)[0]
+    _, k, v = synth.gaussian(B, S, Hkv, dqk, 128, seed + 1)
+    return q, k, v
+
+
+def _expand_heads_gpu(t, G):
+    return t.repeat_interleave(G, dim=2).contiguous()
+
+
+@pytest.mark.parametrize("B,H,Hkv,S,dqk,p_mode,layout", [
+    (2, 4, 2, 768, 128, None, "bshd"),      # GQA G=2, odd tile count
+    (1, 8, 1, 512, 128, None, "bhsd"),      # MQA G=8, BHSD
+    (1, 4, 4, 1024, 128, None, "padded"),   # MHA, padded head stride
+    (2, 4, 2, 512, 192, None, "bhsd"),      # MLA shape, exact P, GQA
+    (1, 2, 2, 1024, 128, cfa.P_EXACT, "bshd"),
+    (1, 2, 1, 768, 192, cfa.P_LEAN, "bhsd"),
+])
+def test_fp8_ex(B, H, Hkv, S, dqk, p_mode, layout):
+    _case("fp8_ex", B, H, Hkv, S, dqk, p_mode, layout)
+    G = H // Hkv
+    q, k, v = _inputs(B, H, Hkv, S, dqk, seed=7 * S + H + dqk)
+    gq = [cfa.quantize_e4m3(torch.from_numpy(x).to(DEV)) for x in (q, k, v)]
+    # codes handled as uint8 (the binding accepts them; float8 tensors lack some copy kernels)
+    (qg, dq), (kg, dk), (vg, dv) = [(c.view(torch.uint8), float(d.item())) for c, d in gq]
+    (qc, dq_o), (kc, dk_o), (vc, dv_o) = [oracle.quantize_e4m3(x) for x in (q, k, v)]
+    assert (dq, dk, dv) == (dq_o, dk_o, dv_o)
+    c = 1.0 / math.sqrt(dqk)
+    qL, kL, vL = (_relayout(t, layout) for t in (qg, kg, vg))
+    out = _out_like(B, S, H, layout)
+    lse = torch.full((B, H, S), float("nan"), dtype=torch.float32, device=DEV)
+    cfa.attn_fwd_causal_fp8_ex(qL, kL, vL, dq, dk, dv, softmax_scale=c, p_mode=p_mode, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out.float()).any() and not torch.isnan(lse).any()
+
+    # bit-exact against the dense MHA path on expanded heads (same P mode)
+    exact_p = (p_mode == cfa.P_EXACT) or (p_mode is None and dqk == 192)
+    ref_out = torch.empty((B, S, H, 128), dtype=torch.bfloat16, device=DEV)
+    ref_lse = torch.empty((B, H, S), dtype=torch.float32, device=DEV)
+    kE, vE = _expand_heads_gpu(kg, G), _expand_heads_gpu(vg, G)
+    cfa.attn_fwd_causal_fp8_ex(qg.contiguous(), kE, vE, dq, dk, dv, softmax_scale=c,
+                               p_mode=cfa.P_EXACT if exact_p else cfa.P_LEAN, out=ref_out, lse=ref_lse)
+    torch.cuda.synchronize()
+    assert torch.equal(out.contiguous().view(torch.int16), ref_out.view(torch.int16))
+    assert torch.equal(lse, ref_lse)
+
+    # against the oracle on expanded heads
+    kcE, vcE = np.repeat(kc, G, axis=2), np.repeat(vc, G, axis=2)
+    scheme = oracle.Fp8Scheme(exact_p=exact_p)
+    groups = all_groups(B, H, S)
+    emu = oracle.emulate_fp8(qc, kcE, vcE, dq=dq, dk=dk, dv=dv, c=c, scheme=scheme, groups=groups)
+    rows = oracle.group_rows(groups, scheme.group)
+    ex, ex_lse = oracle.attn_exact(qc, kcE, vcE, dtype="fp8", c=c, dq=dq, dk=dk, dv=dv, rows=rows)
+    got, glse = gpu_rows(out.contiguous(), rows), lse_rows(lse, rows)
+    res = {"emu_maxabs": float(np.max(np.abs(got - emu["out"]))), "emu_rms": rms_rel(got, emu["out"]),
+           "fp64_rms": rms_rel(got, ex), "lse_emu": float(np.max(np.abs(glse - emu["lse"]))),
+           "lse_fp64": float(np.max(np.abs(glse - ex_lse)))}
+    print("RESULT", res, flush=True)
+    assert res["emu_maxabs"] <= TOL_EMU_MAXABS and res["emu_rms"] <= TOL_EMU_RMS, res
+    assert res["fp64_rms"] <= TOL_FP64_RMS_FP8, res
+    assert res["lse_emu"] <= LSE_EMU_NATS and res["lse_fp64"] <= LSE_FP64_NATS, res
+
+
+def test_fp8_ex_matches_basic_entry_points():
+    """Dense BSHD, H_kv = H and the default P mode: identical to attn_fwd_causal_fp8 / _mla."""
+    for dqk, basic in ((128, cfa.attn_fwd_causal_fp8), (192, cfa.attn_fwd_causal_mla)):
+        B, H, S = 1, 3, 512
+        _case("fp8_ex vs basic", dqk, B, H, S)
+        q, k, v = synth.gaussian(B, S, H, dqk, 128, 11)
+        (qg, dq), (kg, dk), (vg, dv) = [(c_, float(d_.item())) for c_, d_ in
+                                        (cfa.quantize_e4m3(torch.from_numpy(x).to(DEV)) for x in (q, k, v))]
+        o1, l1 = basic(qg, kg, vg, dq, dk, dv)
+        o2, l2 = cfa.attn_fwd_causal_fp8_ex(qg, kg, vg, dq, dk, dv)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("B,H,Hkv,S,layout", [(2, 4, 2, 768, "bhsd"), (1, 8, 2, 1024, "padded"),
+                                              (1, 4, 1, 512, "bshd")])
+def test_bf16_ex(B, H, Hkv, S, layout):
+    _case("bf16_ex", B, H, Hkv, S, layout)
+    G = H // Hkv
+    q, k, v = _inputs(B, H, Hkv, S, 128, seed=5 * S + H)
+    qg, kg, vg = (cfa.round_bf16(torch.from_numpy(x).to(DEV)) for x in (q, k, v))
+    qb, kb, vb = (oracle.bf16_rne(x) for x in (q, k, v))
+    c = 1.0 / math.sqrt(128)
+    qL, kL, vL = (_relayout(t, layout) for t in (qg, kg, vg))
+    out = _out_like(B, S, H, layout)
+    lse = torch.full((B, H, S), float("nan"), dtype=torch.float32, device=DEV)
+    cfa.attn_fwd_causal_bf16_ex(qL, kL, vL, softmax_scale=c, out=out, lse=lse)
+    ref_out, ref_lse = cfa.attn_fwd_causal_bf16(qg, _expand_heads_gpu(kg, G), _expand_heads_gpu(vg, G),
+                                                softmax_scale=c)
+    torch.cuda.synchronize()
+    assert torch.equal(out.contiguous().view(torch.int16), ref_out.view(torch.int16))
+    assert torch.equal(lse, ref_lse)
+    rows = oracle.group_rows(all_groups(B, H, S), 32)
+    ex, ex_lse = oracle.attn_exact(qb, np.repeat(kb, G, axis=2), np.repeat(vb, G, axis=2), dtype="bf16", c=c,
+                                   rows=rows)
+    got, glse = gpu_rows(out.contiguous(), rows), lse_rows(lse, rows)
+    res = {"fp64_rms": rms_rel(got, ex), "lse_fp64": float(np.max(np.abs(glse - ex_lse)))}
+    print("RESULT", res, flush=True)
+    assert res["fp64_rms"] <= TOL_FP64_RMS_BF16, res
+    assert res["lse_fp64"] <= 1e-3 + 1e-6 * np.max(np.abs(ex_lse)), res
