@@ -185,6 +185,29 @@ def run_fp8(torch, cfa, kind, synth_fn, B, H, S, dqk, warmup, steps, seed=0, sus
     return res
 
 
+def run_fp8_ex(torch, cfa, B, H, Hkv, S, dqk, p_mode, warmup, steps, seed=0):
+    """FP8 through the general entry point: grouped-query k/v (Hkv heads) and a P mode."""
+    import synth
+    log(f"fp8_ex B={B} H={H} Hkv={Hkv} S={S} d_qk={dqk} p_mode={p_mode}: generating inputs")
+    dev = torch.device("cuda:0")
+    q = synth.gaussian(B, S, H, dqk, 128, seed)[0]
+    _, k, v = synth.gaussian(B, S, Hkv, dqk, 128, seed + 1)
+    codes, ds = [], []
+    for x in (q, k, v):
+        c, d = cfa.quantize_e4m3(torch.from_numpy(x).to(dev))
+        codes.append(c)
+        ds.append(float(d.item()))
+    del q, k, v
+    out = torch.empty((B, S, H, 128), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    fn = lambda: cfa.attn_fwd_causal_fp8_ex(codes[0], codes[1], codes[2], ds[0], ds[1], ds[2], p_mode=p_mode,
+                                            out=out, lse=lse)
+    ms = time_launches(torch, fn, warmup, steps)
+    F = flops(B, H, S, dqk, 128)
+    log(f"fp8_ex B={B} H={H} Hkv={Hkv} S={S} d_qk={dqk}: {ms:.4f} ms/launch")
+    return {"ms": ms, "tflops": F / (ms * 1e-3) / 1e12}
+
+
 def run_bf16(torch, cfa, B, H, S, warmup, steps, seed=0, sustained=False):
     import synth
     log(f"bf16 B={B} H={H} S={S}: generating inputs")
@@ -322,6 +345,12 @@ def main():
         also["mla_fp8_B1_H16_S32768_192_128"] = {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4),
                                                   "pct_fp8_peak": round(100 * r["tflops"] / PEAK_TFLOPS["fp8"], 2),
                                                   "sustained": r.get("sustained")}
+        r = run_fp8_ex(torch, cfa, 1, 16, 16, 32768, 192, cfa.P_LEAN, wb, sb)
+        also["mla_fp8_leanP_B1_H16_S32768_192_128"] = {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4),
+                                                        "pct_fp8_peak": round(100 * r["tflops"] / PEAK_TFLOPS["fp8"], 2)}
+        r = run_fp8_ex(torch, cfa, 1, 32, 8, 32768, 128, cfa.P_LEAN, wb, sb)
+        also["fp8_gqa_B1_H32_Hkv8_S32768_d128"] = {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4),
+                                                    "pct_fp8_peak": round(100 * r["tflops"] / PEAK_TFLOPS["fp8"], 2)}
         r = run_fp8(torch, cfa, "fp8", synth.activation_like, 1, 32, 16384, 128, wb, sb)
         also["fp8_activation_like_B1_H32_S16384_d128"] = {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4)}
         result["also"] = also
