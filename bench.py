@@ -208,20 +208,23 @@ def run_fp8_ex(torch, cfa, B, H, Hkv, S, dqk, p_mode, warmup, steps, seed=0):
     return {"ms": ms, "tflops": F / (ms * 1e-3) / 1e12}
 
 
-def run_bf16(torch, cfa, B, H, S, warmup, steps, seed=0, sustained=False):
+def run_bf16(torch, cfa, B, H, S, warmup, steps, seed=0, sustained=False, dqk=128):
     import synth
-    log(f"bf16 B={B} H={H} S={S}: generating inputs")
-    q, k, v = synth.gaussian(B, S, H, 128, 128, seed)
+    log(f"bf16 B={B} H={H} S={S} d_qk={dqk}: generating inputs")
+    q, k, v = synth.gaussian(B, S, H, dqk, 128, seed)
     dev = torch.device("cuda:0")
     tens = [torch.from_numpy(x).to(dev) for x in (q, k, v)]
     del q, k, v
     qg, kg, vg = (cfa.round_bf16(t) for t in tens)
     out = torch.empty((B, S, H, 128), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
-    fn = lambda: cfa.attn_fwd_causal_bf16(qg, kg, vg, out=out, lse=lse)
+    if dqk == 128:
+        fn = lambda: cfa.attn_fwd_causal_bf16(qg, kg, vg, out=out, lse=lse)
+    else:
+        fn = lambda: cfa.attn_fwd_causal_bf16_ex(qg, kg, vg, out=out, lse=lse)
     ms = time_launches(torch, fn, warmup, steps)
-    F = flops(B, H, S, 128, 128)
-    log(f"bf16 B={B} H={H} S={S}: {ms:.4f} ms/launch")
+    F = flops(B, H, S, dqk, 128)
+    log(f"bf16 B={B} H={H} S={S} d_qk={dqk}: {ms:.4f} ms/launch")
     res = {"ms": ms, "tflops": F / (ms * 1e-3) / 1e12}
     if sustained:
         res["sustained"] = sustained_window(torch, fn, F)
@@ -345,6 +348,9 @@ def main():
         also["mla_fp8_B1_H16_S32768_192_128"] = {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4),
                                                   "pct_fp8_peak": round(100 * r["tflops"] / PEAK_TFLOPS["fp8"], 2),
                                                   "sustained": r.get("sustained")}
+        r = run_bf16(torch, cfa, 1, 16, 32768, wb, sb, dqk=192)
+        also["mla_bf16_B1_H16_S32768_192_128"] = {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4),
+                                                   "pct_bf16_peak": round(100 * r["tflops"] / PEAK_TFLOPS["bf16"], 2)}
         r = run_fp8_ex(torch, cfa, 1, 16, 16, 32768, 192, cfa.P_LEAN, wb, sb)
         also["mla_fp8_leanP_B1_H16_S32768_192_128"] = {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4),
                                                         "pct_fp8_peak": round(100 * r["tflops"] / PEAK_TFLOPS["fp8"], 2)}

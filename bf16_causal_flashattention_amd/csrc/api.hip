@@ -158,7 +158,7 @@ int run_fp8(const Problem& p, float qd, float kd, float vd, float sm, int p_mode
 }
 
 int run_bf16(const Problem& p, float sm, void* stream) {
-  if (p.dqk != 128 || p.dv != 128) return ATTN_ERR_SHAPE;
+  if ((p.dqk != 128 && p.dqk != 192) || p.dv != 128) return ATTN_ERR_SHAPE;
   int rc = check_attn(p, 2);
   if (rc == 1) return ATTN_OK;
   if (rc != ATTN_OK) return rc;
@@ -182,7 +182,7 @@ int run_bf16(const Problem& p, float sm, void* stream) {
   a.mk = tmap(p.sk, 2);
   a.mv = tmap(p.sv, 2);
   a.mo = tmap(p.so, 2);
-  const hipError_t e = cfa::launch_bf16(a, grid_for(p.B, p.H, p.S, ncu), (hipStream_t)stream);
+  const hipError_t e = cfa::launch_bf16(a, p.dqk, grid_for(p.B, p.H, p.S, ncu), (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -227,6 +227,7 @@ int attn_fwd_causal_fp8_debug(const void* q, const void* k, const void* v, void*
 
 int attn_fwd_causal_bf16(const void* q, const void* k, const void* v, void* out, float* lse,
                          float softmax_scale, int B, int H, int S, int d_qk, int d_v, void* stream) {
+  if (d_qk != 128) return ATTN_ERR_SHAPE;
   const Problem p = make_problem(q, k, v, out, lse, B, H, H, S, d_qk, d_v, nullptr, nullptr, nullptr, nullptr);
   return run_bf16(p, softmax_scale, stream);
 }

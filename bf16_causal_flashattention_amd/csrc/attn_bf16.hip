@@ -4,7 +4,7 @@
 //   Sec. II-B  base-2 online softmax over 64-key blocks, LSE output;
 //   Sec. IV-A  8 waves x 32 query rows, S^T = K Q^T so each lane holds one query's
 //              scores, causal pairing, persistent grid, chiplet map, lazy rescaling
-//              with tau = 0.5 (the BF16 value at d = 128);
+//              with tau = 0.5 at d_qk = 128 and 8 at the MLA shape d_qk = 192;
 //   Sec. VI-A  dead-block skip: in the diagonal blocks a wave skips the 64-key blocks
 //              that the causal mask hides from all its rows (loads and barriers still run);
 //   Sec. IV-D  the 8-wave ping-pong of the BF16 d = 128 kernel: the two waves of a SIMD
@@ -31,29 +31,37 @@ namespace cfa {
 
 namespace {
 
-constexpr float kTauBf16 = 0.5f;
+// lazy-rescale threshold in base-2 units of the score (Sec. IV-A): 0.5 at d_qk = 128 and 8
+// at the MLA shape d_qk = 192 (p stays below 2^8 in fp32 between rescales)
+template <int DQK>
+constexpr float kTauBf16 = DQK == 128 ? 0.5f : 8.0f;
 constexpr float kLn2 = 0.69314718055994530942f;
 
 // LDS: two K slots then three V slots, each a run of 16-byte cells filled by DMA
 // (global_load_lds: lane L of a wave writes cell base + L); pad cells receive a copy of a
 // data cell of the same row (no per-lane masking) and are never read.
 //   K slot: row 32*(key/32) + key_perm_bf16(key%32) holds key `key` (key_perm_bf16 is an
-//           involution), 17 cells (272 bytes) per row, so lane i reads row 32u + i, which
-//           holds key 32u + key_perm_bf16(i).
+//           involution), d_qk/8 + 1 cells per row (272 bytes at d_qk = 128, 400 at 192;
+//           both keep each 16-lane group of a 16-byte read on distinct banks), so lane i
+//           reads row 32u + i, which holds key 32u + key_perm_bf16(i).
 //   V slot: row r holds V[key0 + r][0..127], 18 cells (288 bytes) per row; the PV operand
 //           (V^T) comes from LDS transpose reads.
 constexpr int kBlk = 64;  // keys per block (max update, ping-pong phase and LDS slot)
-constexpr int kKSpr = 17;
-constexpr int kKStride = 16 * kKSpr;
-constexpr int kKCells = kBlk * kKSpr;
-constexpr int kKSlot = 16 * kKCells;
-constexpr int kVSpr = 18;
-constexpr int kVStride = 16 * kVSpr;
-constexpr int kVCells = kBlk * kVSpr;
-constexpr int kVSlot = 16 * kVCells;
-constexpr int kVBase = 2 * kKSlot;
-constexpr int kLdsBytes = 2 * kKSlot + 3 * kVSlot;
-constexpr int kRounds = (kVCells + 255) / 256;  // >= (kKCells + 255) / 256
+template <int DQK>
+struct Bf16Lds {
+  static constexpr int kKCols = DQK / 8;  // 16-byte data cells per K row
+  static constexpr int kKSpr = kKCols + 1;
+  static constexpr int kKStride = 16 * kKSpr;
+  static constexpr int kKCells = kBlk * kKSpr;
+  static constexpr int kKSlot = 16 * kKCells;
+  static constexpr int kVSpr = 18;
+  static constexpr int kVStride = 16 * kVSpr;
+  static constexpr int kVCells = kBlk * kVSpr;
+  static constexpr int kVSlot = 16 * kVCells;
+  static constexpr int kVBase = 2 * kKSlot;
+  static constexpr int kLdsBytes = 2 * kKSlot + 3 * kVSlot;
+  static constexpr int kRounds = ((kKCells > kVCells ? kKCells : kVCells) + 255) / 256;
+};
 
 // max of two floats that are never NaN, as one v_max_f32 (fmaxf would first quiet both
 // operands, which the compiler cannot prove unnecessary for MFMA and permlane results)
@@ -79,8 +87,15 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+template <int DQK>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
+  using L = Bf16Lds<DQK>;
+  constexpr int kKStride = L::kKStride, kKCells = L::kKCells, kKSlot = L::kKSlot, kKSpr = L::kKSpr;
+  constexpr int kVStride = L::kVStride, kVCells = L::kVCells, kVSlot = L::kVSlot, kVSpr = L::kVSpr;
+  constexpr int kVBase = L::kVBase, kRounds = L::kRounds;
+  constexpr int QM = DQK / 16;  // 16-deep k steps of S^T = K Q^T
+  constexpr float kTau = kTauBf16<DQK>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[L::kLdsBytes];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in SGPRs
@@ -110,7 +125,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
     const int cell = 256 * p + st;
     if (stage_k) {
       const int row = (cell / kKSpr) & (kBlk - 1), col = cell % kKSpr;
-      st_goff[p] = ((row & ~31) | key_perm_bf16(row & 31)) * krs + 16 * (col < 16 ? col : 0);
+      st_goff[p] = ((row & ~31) | key_perm_bf16(row & 31)) * krs + 16 * (col < L::kKCols ? col : 0);
     } else {
       const int row = (cell / kVSpr) & (kBlk - 1), col = cell % kVSpr;
       st_goff[p] = row * vrs + 16 * (col < 16 ? col : 0);
@@ -144,11 +159,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
           if (256 * p + 64 * wq < st_cells) dma16(src + st_goff[p], dst + 4096 * p);
       };
 
-      v4i qop[8];  // Q^T operand: lane holds Q[qrow][16m + 8hh .. +8]
+      v4i qop[QM];  // Q^T operand: lane holds Q[qrow][16m + 8hh .. +8]
       {
         const uint8_t* qp = qbh + (int64_t)qrow * a.mq.ss + 16 * hh;
 #pragma unroll
-        for (int m = 0; m < 8; ++m) qop[m] = *(const v4i*)(qp + 32 * m);
+        for (int m = 0; m < QM; ++m) qop[m] = *(const v4i*)(qp + 32 * m);
       }
       v16f oacc[4];
 #pragma unroll
@@ -163,20 +178,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
       auto qk = [&](int blk) {
         const uint8_t* sk = smem + (blk & 1) * kKSlot + k_rd;
         auto kread = [&](int t) { return *(const v4i*)(sk + 32 * (t & 1) * kKStride + 32 * (t >> 1)); };
-        constexpr int D = 3;  // operand reads in flight ahead of the MFMAs
+        constexpr int D = 3;       // operand reads in flight ahead of the MFMAs
+        constexpr int N = 2 * QM;  // MFMAs
         v4i kop[D + 1];
 #pragma unroll
         for (int t = 0; t < D; ++t) kop[t] = kread(t);
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
+        for (int t = 0; t < N; ++t) {
           const int u = t & 1, mm = t >> 1;
-          if (t + D < 16) kop[(t + D) % (D + 1)] = kread(t + D);
+          if (t + D < N) kop[(t + D) % (D + 1)] = kread(t + D);
           sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(kop[t % (D + 1)]), as_bf(qop[mm]),
                                                             mm == 0 ? zero16 : sacc[u], 0, 0, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x100, D, 0);
 #pragma unroll
-        for (int t = 0; t < 16 - D; ++t) {
+        for (int t = 0; t < N - D; ++t) {
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
@@ -209,7 +225,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
           m = tmax;
         } else {
           const float M = fmaxf(m, tmax);
-          if (__any((M - m) >= kTauBf16)) {  // O and l hold blocks <= blk-1
+          if (__any((M - m) >= kTau)) {  // O and l hold blocks <= blk-1
             const float f = __builtin_amdgcn_exp2f(m - M);
             l *= f;
             m = M;
@@ -316,8 +332,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
 
 }  // namespace
 
-hipError_t launch_bf16(const Bf16Args& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
+hipError_t launch_bf16(const Bf16Args& a, int dqk, int grid, hipStream_t stream) {
+  if (dqk == 128)
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<128>), dim3(grid), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<192>), dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -29,8 +29,8 @@ struct Fp8Args {
 };
 
 struct Bf16Args {
-  const uint16_t* q;  // bf16 bits, [B][S][H][128] through mq
-  const uint16_t* k;  // [B][S][H_kv][128] through mk
+  const uint16_t* q;  // bf16 bits, [B][S][H][d_qk] through mq (d_qk = 128 or 192)
+  const uint16_t* k;  // [B][S][H_kv][d_qk] through mk
   const uint16_t* v;  // [B][S][H_kv][128] through mv
   uint16_t* out;      // [B][S][H][128] through mo
   float* lse;
@@ -41,7 +41,7 @@ struct Bf16Args {
 };
 
 hipError_t launch_fp8(const Fp8Args& a, int dqk, bool exact_p, bool debug, int grid, hipStream_t stream);
-hipError_t launch_bf16(const Bf16Args& a, int grid, hipStream_t stream);
+hipError_t launch_bf16(const Bf16Args& a, int dqk, int grid, hipStream_t stream);
 hipError_t launch_quantize_e4m3(const float* x, int64_t n, uint8_t* codes, float* descale, uint32_t* ws,
                                 hipStream_t stream);
 hipError_t launch_round_bf16(const float* x, int64_t n, uint16_t* out, hipStream_t stream);

@@ -112,8 +112,10 @@ int attn_fwd_causal_fp8_ex(const void* q, const void* k, const void* v, void* ou
                            const attn_strides* v_strides, const attn_strides* out_strides, int p_mode,
                            void* stream);
 
-/* General BF16 entry point: d_qk = d_v = 128 with grouped-query heads and strides as for
- * attn_fwd_causal_fp8_ex (strides in bf16 elements). */
+/* General BF16 entry point: d_qk = 128, or the MLA shape d_qk = 192, with d_v = 128;
+ * grouped-query heads and strides as for attn_fwd_causal_fp8_ex (strides in bf16
+ * elements).  At d_qk = 192 the lazy-rescale threshold is 8 binades, as in the paper's
+ * BF16 MLA kernel (Sec. IV-A). */
 int attn_fwd_causal_bf16_ex(const void* q, const void* k, const void* v, void* out, float* lse,
                             float softmax_scale, int B, int H, int H_kv, int S, int d_qk, int d_v,
                             const attn_strides* q_strides, const attn_strides* k_strides,

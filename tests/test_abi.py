@@ -127,7 +127,8 @@ def test_ex_p_mode_and_head_dims():
     assert _fp8_ex(pm=-2) == -5
     assert _fp8_ex(dqk=192, pm=5) == -5
     assert _fp8_ex(dqk=64) == -2
-    assert _bf16_ex(dqk=192) == -2
+    assert _bf16_ex(dqk=64) == -2
+    assert _bf16_ex(dqk=192, dv=64) == -2
 
 
 def test_ex_bhsd_extent_checked():

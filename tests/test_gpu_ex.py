@@ -124,24 +124,46 @@ def test_fp8_ex_matches_basic_entry_points():
         assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("B,H,Hkv,S,layout", [(2, 4, 2, 768, "bhsd"), (1, 8, 2, 1024, "padded"),
-                                              (1, 4, 1, 512, "bshd")])
-def test_bf16_ex(B, H, Hkv, S, layout):
-    _case("bf16_ex", B, H, Hkv, S, layout)
+@pytest.mark.parametrize("B,H,Hkv,S,dqk,layout", [(2, 4, 2, 768, 128, "bhsd"), (1, 8, 2, 1024, 128, "padded"),
+                                                  (1, 4, 1, 512, 128, "bshd"), (1, 2, 2, 1024, 192, "bshd"),
+                                                  (2, 4, 2, 768, 192, "bhsd"), (1, 4, 1, 512, 192, "padded")])
+def test_bf16_ex(B, H, Hkv, S, dqk, layout):
+    _case("bf16_ex", B, H, Hkv, S, dqk, layout)
+    q, k, v = _inputs(B, H, Hkv, S, dqk, seed=5 * S + H + dqk)
+    _bf16_ex_check(q, k, v, layout)
+
+
+@pytest.mark.parametrize("name", ["rising_logits", "sink_flat_tail", "stepped_max", "logit_sd_16"])
+def test_bf16_mla_stress(name):
+    """BF16 at the MLA shape (lazy threshold 8 binades) on the stress inputs: the rescale
+    path and far-below-maximum blocks against exact fp64."""
+    B, H, S = 1, 2, 1024
+    _case("bf16 mla stress", name, B, H, S)
+    q, k, v = synth.STRESS[name](B, S, H, 192, 128, 33)
+    _bf16_ex_check(q, k, v, "bshd")
+
+
+def _bf16_ex_check(q, k, v, layout):
+    B, S, H, dqk = q.shape
+    Hkv = k.shape[2]
     G = H // Hkv
-    q, k, v = _inputs(B, H, Hkv, S, 128, seed=5 * S + H)
-    qg, kg, vg = (cfa.round_bf16(torch.from_numpy(x).to(DEV)) for x in (q, k, v))
+    qg, kg, vg = (cfa.round_bf16(torch.from_numpy(np.ascontiguousarray(x)).to(DEV)) for x in (q, k, v))
     qb, kb, vb = (oracle.bf16_rne(x) for x in (q, k, v))
-    c = 1.0 / math.sqrt(128)
+    c = 1.0 / math.sqrt(dqk)
     qL, kL, vL = (_relayout(t, layout) for t in (qg, kg, vg))
     out = _out_like(B, S, H, layout)
     lse = torch.full((B, H, S), float("nan"), dtype=torch.float32, device=DEV)
     cfa.attn_fwd_causal_bf16_ex(qL, kL, vL, softmax_scale=c, out=out, lse=lse)
-    ref_out, ref_lse = cfa.attn_fwd_causal_bf16(qg, _expand_heads_gpu(kg, G), _expand_heads_gpu(vg, G),
-                                                softmax_scale=c)
+    ref_out, ref_lse = cfa.attn_fwd_causal_bf16_ex(qg, _expand_heads_gpu(kg, G), _expand_heads_gpu(vg, G),
+                                                   softmax_scale=c)
     torch.cuda.synchronize()
+    assert not torch.isnan(out.float()).any() and not torch.isnan(lse).any()
     assert torch.equal(out.contiguous().view(torch.int16), ref_out.view(torch.int16))
     assert torch.equal(lse, ref_lse)
+    if dqk == 128 and G == 1:
+        o2, l2 = cfa.attn_fwd_causal_bf16(qg, kg, vg, softmax_scale=c)
+        torch.cuda.synchronize()
+        assert torch.equal(o2.view(torch.int16), ref_out.view(torch.int16)) and torch.equal(l2, ref_lse)
     rows = oracle.group_rows(all_groups(B, H, S), 32)
     ex, ex_lse = oracle.attn_exact(qb, np.repeat(kb, G, axis=2), np.repeat(vb, G, axis=2), dtype="bf16", c=c,
                                    rows=rows)
