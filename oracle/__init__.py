@@ -61,6 +61,8 @@ def lib():
         L.orc_bf16_rne.argtypes = [ctypes.c_float]
         L.orc_quantize_e4m3.restype = ctypes.c_float
         L.orc_quantize_e4m3.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        L.orc_quantize_e4m3_f64.restype = ctypes.c_float
+        L.orc_quantize_e4m3_f64.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         L.orc_leanp_code.restype = ctypes.c_int
         L.orc_leanp_code.argtypes = [ctypes.c_double, ctypes.c_int, ctypes.c_double]
         L.orc_exactp_code.restype = ctypes.c_int
@@ -120,6 +122,69 @@ def quantize_e4m3(x: np.ndarray):
     codes = np.empty(x.shape, dtype=np.uint8)
     ds = lib().orc_quantize_e4m3(_ptr(x), x.size, _ptr(codes))
     return codes, float(ds)
+
+
+def quantize_e4m3_f64(x: np.ndarray):
+    """The per-tensor quantiser on fp64 values (no fp32 rounding before the e4m3 rounding)."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    codes = np.empty(x.shape, dtype=np.uint8)
+    ds = lib().orc_quantize_e4m3_f64(_ptr(x), x.size, _ptr(codes))
+    return codes, float(ds)
+
+
+# ----------------------------------------------------------------------------- rotation
+# Paper Sec. V-E, "Rotation and K smoothing": after RoPE, Q and K are multiplied by the
+# same orthogonal R = diag(s) (C_m kron H_{D/m}), s random signs, H the normalised
+# Sylvester-Hadamard matrix, C_m the orthonormal DCT-II; m = 1 for D = 128 and m = 3 for
+# D = 192.  K smoothing subtracts the mean key of each head over the sequence before the
+# rotation.  FP8 scales are taken after the rotation; V and O are not rotated.
+# Reading of the Kronecker indices: element (a, b) -> (a', b') of C kron H is
+# C[a, a'] H[b, b'] with a row/column index a*(D/m) + b, and C[k, n] is the DCT-II
+# coefficient of frequency k at sample n (the matrix used as the left factor of kron).
+
+def hadamard(n: int) -> np.ndarray:
+    """Normalised Sylvester-Hadamard matrix of size n (a power of two), fp64."""
+    assert n >= 1 and n & (n - 1) == 0
+    h = np.ones((1, 1))
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h / np.sqrt(n)
+
+
+def dct2(m: int) -> np.ndarray:
+    """Orthonormal DCT-II matrix C[k, n] = a_k cos(pi (2n + 1) k / (2m)), a_0 = sqrt(1/m),
+    a_k = sqrt(2/m) otherwise."""
+    k = np.arange(m)[:, None]
+    n = np.arange(m)[None, :]
+    a = np.where(k == 0, np.sqrt(1.0 / m), np.sqrt(2.0 / m))
+    return a * np.cos(np.pi * (2 * n + 1) * k / (2 * m))
+
+
+def rotation(signs) -> np.ndarray:
+    """R = diag(signs) (C_m kron H_{D/m}) with m = 1 when D is a power of two, else 3."""
+    s = np.asarray(signs, dtype=np.float64)
+    D = s.size
+    m = 1 if D & (D - 1) == 0 else 3
+    assert D % m == 0 and (D // m) & (D // m - 1) == 0
+    return np.diag(s) @ np.kron(dct2(m), hadamard(D // m))
+
+
+def key_mean(k: np.ndarray) -> np.ndarray:
+    """Mean key of each head over the sequence: k [B][S][H][D] -> [B][H][D], fp64."""
+    return np.asarray(k, dtype=np.float64).mean(axis=1)
+
+
+def rotate(x: np.ndarray, signs, mean: np.ndarray = None) -> np.ndarray:
+    """(x - mean) R for x [B][S][H][D] (mean [B][H][D] or None), fp64."""
+    y = np.asarray(x, dtype=np.float64)
+    if mean is not None:
+        y = y - np.asarray(mean, dtype=np.float64)[:, None, :, :]
+    return y @ rotation(signs)
+
+
+def rotate_quantize_e4m3(x: np.ndarray, signs, mean: np.ndarray = None):
+    """Rotation (and optional K smoothing) in fp64, then the per-tensor quantiser."""
+    return quantize_e4m3_f64(rotate(x, signs, mean))
 
 
 def leanp_code(x: float, sigma: int = SIGMA, beta: float = BETA) -> int:

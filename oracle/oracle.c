@@ -17,6 +17,7 @@
  *   orc_e4m3_rne        round a real to e4m3, nearest-even, saturating to +-448
  *   orc_bf16_rne        round an fp32 to bf16, nearest-even
  *   orc_quantize_e4m3   per-tensor power-of-two scaled quantiser   paper Sec. V-E, fn 17
+ *   orc_quantize_e4m3_f64  the same quantiser on fp64 inputs (rotated Q, K; Sec. V-E)
  *   orc_leanp_code      lean-P code of x = log2 p (ideal, fp64)    paper Sec. IV-B1, Eq. 2
  *   orc_exactp_code     exact-P code of x (round 2^(x+sigma))      paper Sec. IV-B1
  *   orc_attn_exact      exact causal softmax attention in fp64     paper Sec. II-B (definition)
@@ -106,12 +107,7 @@ double orc_bf16_value(uint16_t b) {
  * the largest power of two 2^k with amax * 2^k <= 448, so nothing saturates; k is
  * clamped to [-126, 126] so that the fp32 descale 2^-k is a normal number; an
  * all-zero tensor gets k = 0.  Returns the descale 2^-k (exact in fp32).       */
-float orc_quantize_e4m3(const float* x, int64_t n, uint8_t* codes) {
-  double amax = 0.0;
-  for (int64_t i = 0; i < n; ++i) {
-    double a = fabs((double)x[i]);
-    if (a > amax) amax = a;
-  }
+static int orc_pow2_exponent(double amax) {
   int k = 0;
   if (amax > 0.0) {
     k = (int)floor(log2(448.0 / amax));
@@ -120,8 +116,33 @@ float orc_quantize_e4m3(const float* x, int64_t n, uint8_t* codes) {
     if (k > 126) k = 126;
     if (k < -126) k = -126;
   }
+  return k;
+}
+
+float orc_quantize_e4m3(const float* x, int64_t n, uint8_t* codes) {
+  double amax = 0.0;
+  for (int64_t i = 0; i < n; ++i) {
+    double a = fabs((double)x[i]);
+    if (a > amax) amax = a;
+  }
+  const int k = orc_pow2_exponent(amax);
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i) codes[i] = (uint8_t)orc_e4m3_rne(ldexp((double)x[i], k));
+  return (float)ldexp(1.0, -k);
+}
+
+/* The same quantiser applied to fp64 values, for inputs the oracle itself computes in
+ * fp64 (the rotated Q and K of paper Sec. V-E, "Rotation and K smoothing", whose FP8
+ * scales come after the rotation). */
+float orc_quantize_e4m3_f64(const double* x, int64_t n, uint8_t* codes) {
+  double amax = 0.0;
+  for (int64_t i = 0; i < n; ++i) {
+    double a = fabs(x[i]);
+    if (a > amax) amax = a;
+  }
+  const int k = orc_pow2_exponent(amax);
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) codes[i] = (uint8_t)orc_e4m3_rne(ldexp(x[i], k));
   return (float)ldexp(1.0, -k);
 }
 
