@@ -231,6 +231,38 @@ def run_bf16(torch, cfa, B, H, S, warmup, steps, seed=0, sustained=False, dqk=12
     return res
 
 
+def run_rotate_prepass(torch, cfa, B, H, S, D, warmup, steps, seed=0):
+    """Input preparation with rotation and K smoothing (q, k rotated; k smoothed; v plain)
+    against plain per-tensor quantisation of q, k, v, both on fp32 inputs in HBM.
+    Algorithmic bytes per element: the key mean reads k once (4); each quantiser reads its
+    tensor twice (the per-tensor scale needs max |y| before the first code) and writes
+    one byte (9)."""
+    import synth
+    q, k, v = synth.gaussian(B, S, H, D, D, seed)
+    dev = torch.device("cuda:0")
+    qg, kg, vg = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    del q, k, v
+    sg = torch.from_numpy(np.where(np.random.default_rng(seed).integers(0, 2, D) == 1, 1.0, -1.0)
+                          .astype(np.float32)).to(dev)
+
+    def rotated():
+        cfa.rotate_quantize_e4m3(qg, sg)
+        cfa.rotate_quantize_e4m3(kg, sg, cfa.key_mean(kg))
+        cfa.quantize_e4m3(vg)
+
+    def plain():
+        for t in (qg, kg, vg):
+            cfa.quantize_e4m3(t)
+
+    n = B * S * H * D
+    ms_r = time_launches(torch, rotated, warmup, steps)
+    ms_p = time_launches(torch, plain, warmup, steps)
+    del qg, kg, vg
+    return {"ms": round(ms_r, 4), "ms_plain_quantise": round(ms_p, 4),
+            "hbm_gbs_at_algorithmic_bytes": round(31 * n / (ms_r * 1e-3) / 1e9, 1),
+            "plain_hbm_gbs_at_algorithmic_bytes": round(27 * n / (ms_p * 1e-3) / 1e9, 1)}
+
+
 def cpu_baseline(B, H, S, dqk, budget_s=20.0, seed=0):
     """The oracle's FP8 emulation (mirror mode) timed on host cores over a bounded sample
     of the headline workload: 32-row groups at seeded positions until ~budget_s of work."""
@@ -359,6 +391,8 @@ def main():
                                                     "pct_fp8_peak": round(100 * r["tflops"] / PEAK_TFLOPS["fp8"], 2)}
         r = run_fp8(torch, cfa, "fp8", synth.activation_like, 1, 32, 16384, 128, wb, sb)
         also["fp8_activation_like_B1_H32_S16384_d128"] = {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4)}
+        also["prepass_rotate_smooth_B1_H32_S32768_d128"] = run_rotate_prepass(torch, cfa, 1, 32, 32768, 128, wb, sb)
+        also["prepass_rotate_smooth_B1_H16_S32768_d192"] = run_rotate_prepass(torch, cfa, 1, 16, 32768, 192, wb, sb)
         result["also"] = also
         result["fp8_over_bf16_speedup_S32768"] = round(head["tflops"] / also["bf16_B1_H32_S32768_d128"]["tflops"], 3)
     if not args.no_cpu_baseline:

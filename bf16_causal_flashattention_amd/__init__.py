@@ -12,6 +12,7 @@ Functions mirror the C entry points:
     attn_fwd_causal_fp8_ex(q, k, v, q_descale, k_descale, v_descale, softmax_scale=None, p_mode=None)
     attn_fwd_causal_bf16_ex(q, k, v, softmax_scale=None)
     quantize_e4m3(x) -> (codes, descale)      round_bf16(x) -> bf16 tensor
+    key_mean(k) -> mean [B, H, D]             rotate_quantize_e4m3(x, signs, mean=None) -> (codes, descale)
 Tensors are BSHD: q, k [B, S, H, d_qk], v [B, S, H, d_v]; outputs out [B, S, H, d_v]
 (bfloat16) and lse [B, H, S] (float32).  The *_ex functions take BSHD-shaped views of any
 strided layout (e.g. a BHSD tensor x passed as x.permute(0, 2, 1, 3)) with the head
@@ -66,6 +67,10 @@ def lib():
         L.attn_fwd_causal_bf16_ex.argtypes = [P, P, P, P, P, F, I, I, I, I, I, I, SP, SP, SP, SP, P]
         L.attn_quantize_e4m3.argtypes = [P, I64, P, P, P, P]
         L.attn_round_bf16.argtypes = [P, I64, P, P]
+        L.attn_key_mean_workspace.argtypes = [I, I, I, I]
+        L.attn_key_mean_workspace.restype = I64
+        L.attn_key_mean.argtypes = [P, I, I, I, I, P, P, P]
+        L.attn_rotate_quantize_e4m3.argtypes = [P, P, P, I, I, I, I, P, P, P, P]
         L.attn_default_grid.argtypes = [I, I, I, I]
         L.attn_schedule.argtypes = [I, I, I, I, P, I64]
         L.attn_schedule.restype = I64
@@ -73,7 +78,8 @@ def lib():
         L.attn_status_string.restype = ctypes.c_char_p
         for name in ("attn_fwd_causal_fp8", "attn_fwd_causal_mla", "attn_fwd_causal_fp8_debug",
                      "attn_fwd_causal_bf16", "attn_fwd_causal_fp8_ex", "attn_fwd_causal_bf16_ex",
-                     "attn_quantize_e4m3", "attn_round_bf16", "attn_default_grid"):
+                     "attn_quantize_e4m3", "attn_round_bf16", "attn_default_grid", "attn_key_mean",
+                     "attn_rotate_quantize_e4m3"):
             getattr(L, name).restype = I
         _lib = L
     return _lib
@@ -244,6 +250,46 @@ def quantize_e4m3(x, workspace=None):
         workspace = torch.empty(1, dtype=torch.int32, device=x.device)
     rc = lib().attn_quantize_e4m3(_ptr(x), x.numel(), _ptr(codes), _ptr(descale), _ptr(workspace), _stream())
     _check("attn_quantize_e4m3", rc)
+    return codes.view(torch.float8_e4m3fn), descale
+
+
+def _bshd_f32(x, name):
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous() or x.dim() != 4:
+        raise TypeError(f"{name} must be a contiguous float32 GPU tensor [B, S, H, D]")
+    return x.shape
+
+
+def key_mean(k):
+    """Mean key of each head over the sequence (K smoothing), float32 [B, H, D]."""
+    B, S, H, D = _bshd_f32(k, "k")
+    L = lib()
+    n_ws = L.attn_key_mean_workspace(B, S, H, D)
+    if n_ws < 0:
+        raise AttnError("attn_key_mean_workspace", int(n_ws))
+    mean = torch.empty((B, H, D), dtype=torch.float32, device=k.device)
+    ws = torch.empty(max((int(n_ws) + 7) // 8, 1), dtype=torch.float64, device=k.device)
+    _check("attn_key_mean", L.attn_key_mean(_ptr(k), B, S, H, D, _ptr(mean), _ptr(ws), _stream()))
+    return mean
+
+
+def rotate_quantize_e4m3(x, signs, mean=None, workspace=None):
+    """Rotate rows of x [B, S, H, D] by diag(signs) (C_m kron H_{D/m}) after subtracting
+    mean [B, H, D] (if given), then quantise to e4m3 with one power-of-two scale.
+
+    Returns (codes as float8_e4m3fn with x's shape, descale as a 1-element float32 tensor)."""
+    B, S, H, D = _bshd_f32(x, "x")
+    if signs.dtype != torch.float32 or not signs.is_cuda or signs.shape != (D,) or not signs.is_contiguous():
+        raise TypeError("signs must be a contiguous float32 GPU tensor of D values")
+    if mean is not None and (mean.dtype != torch.float32 or not mean.is_cuda or mean.shape != (B, H, D)
+                             or not mean.is_contiguous()):
+        raise TypeError("mean must be a contiguous float32 GPU tensor [B, H, D]")
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    descale = torch.empty(1, dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(1, dtype=torch.int32, device=x.device)
+    rc = lib().attn_rotate_quantize_e4m3(_ptr(x), _ptr(mean), _ptr(signs), B, S, H, D, _ptr(codes), _ptr(descale),
+                                         _ptr(workspace), _stream())
+    _check("attn_rotate_quantize_e4m3", rc)
     return codes.view(torch.float8_e4m3fn), descale
 
 

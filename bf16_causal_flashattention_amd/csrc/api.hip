@@ -252,6 +252,41 @@ int attn_quantize_e4m3(const float* x, int64_t n, uint8_t* codes, float* descale
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
+int64_t attn_key_mean_workspace(int B, int S, int H, int D) {
+  if (B < 0 || S < 0 || H < 0 || (D != 128 && D != 192)) return ATTN_ERR_SHAPE;
+  return cfa::key_mean_workspace_bytes(B, S, H, D);
+}
+
+int attn_key_mean(const float* k, int B, int S, int H, int D, float* mean, void* workspace, void* stream) {
+  if (B < 0 || S < 0 || H < 0 || (D != 128 && D != 192)) return ATTN_ERR_SHAPE;
+  if (B == 0 || H == 0) return ATTN_OK;
+  if (S == 0) return ATTN_ERR_SHAPE;  // the mean of no keys is undefined
+  if (!k || !mean || !workspace) return ATTN_ERR_NULL;
+  if (!aligned(k, 4) || !aligned(mean, 4) || !aligned(workspace, 8)) return ATTN_ERR_ALIGN;
+  if ((int64_t)B * S * H * D >= (INT64_C(1) << 31) || (int64_t)B * H >= 65536) return ATTN_ERR_RANGE;
+  const hipError_t e = cfa::launch_key_mean(k, B, S, H, D, mean, workspace, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int attn_rotate_quantize_e4m3(const float* x, const float* mean, const float* signs, int B, int S, int H, int D,
+                              uint8_t* codes, float* descale, uint32_t* workspace, void* stream) {
+  if (B < 0 || S < 0 || H < 0 || (D != 128 && D != 192)) return ATTN_ERR_SHAPE;
+  if (!descale || !workspace || !signs) return ATTN_ERR_NULL;
+  const int64_t n = (int64_t)B * S * H * D;
+  if (n > 0 && (!x || !codes)) return ATTN_ERR_NULL;
+  if (!aligned(x, 4) || !aligned(signs, 4) || !aligned(mean, 4) || !aligned(descale, 4) || !aligned(workspace, 4))
+    return ATTN_ERR_ALIGN;
+  if (n >= (INT64_C(1) << 31)) return ATTN_ERR_RANGE;
+  // orthonormal DCT-II of size 3 (the C_m factor at D = 192): C[k][n] = a_k cos(pi (2n+1) k / 6)
+  float c3[9];
+  for (int kk = 0; kk < 3; ++kk)
+    for (int nn = 0; nn < 3; ++nn)
+      c3[3 * kk + nn] = (float)((kk == 0 ? sqrt(1.0 / 3.0) : sqrt(2.0 / 3.0)) * cos(M_PI * (2 * nn + 1) * kk / 6.0));
+  const hipError_t e = cfa::launch_rotate_quantize(x, mean, signs, B, S, H, D, c3, codes, descale, workspace,
+                                                   (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
 int attn_round_bf16(const float* x, int64_t n, uint16_t* out, void* stream) {
   if (n < 0) return ATTN_ERR_ARG;
   if (n == 0) return ATTN_OK;

@@ -139,6 +139,17 @@ __device__ __forceinline__ float sum_with_partner(float x) {
 
 __device__ __forceinline__ float fmax3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
+// Per-tensor power-of-two e4m3 scale: the largest 2^k with amax * 2^k <= 448 (nothing
+// saturates), k clamped to [-126, 126], k = 0 for amax = 0 (Sec. V-E, footnote 17).
+__device__ __forceinline__ int pow2_exponent_e4m3(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int e;
+  const float f = frexpf(amax, &e);  // amax = f 2^e, f in [0.5, 1); 448 = 0.875 2^9
+  int k = (f <= 0.875f) ? 9 - e : 8 - e;
+  k = k > 126 ? 126 : (k < -126 ? -126 : k);
+  return k;
+}
+
 // fp32 -> bf16 bits, round to nearest even (inputs are finite here).
 __device__ __forceinline__ uint32_t bf16_bits_rne(float x) {
   const uint32_t u = __float_as_uint(x);

@@ -33,19 +33,10 @@ __global__ __launch_bounds__(kPrepThreads) void amax_kernel(const float* __restr
   if ((threadIdx.x & 63) == 0) atomicMax(ws, mx);
 }
 
-__device__ __forceinline__ int pow2_exponent(float amax) {
-  if (!(amax > 0.f)) return 0;
-  int e;
-  const float f = frexpf(amax, &e);  // amax = f 2^e, f in [0.5, 1); 448 = 0.875 2^9
-  int k = (f <= 0.875f) ? 9 - e : 8 - e;
-  k = k > 126 ? 126 : (k < -126 ? -126 : k);
-  return k;
-}
-
 __global__ __launch_bounds__(kPrepThreads) void quantize_kernel(const float* __restrict__ x, int64_t n,
                                                                 uint8_t* __restrict__ codes, float* descale,
                                                                 const uint32_t* ws) {
-  const int k = pow2_exponent(__uint_as_float(ws[0]));
+  const int k = pow2_exponent_e4m3(__uint_as_float(ws[0]));
   const float scale = __int_as_float((127 + k) << 23);
   if (blockIdx.x == 0 && threadIdx.x == 0) *descale = __int_as_float((127 - k) << 23);
   const int64_t n4 = n / 4;

@@ -130,6 +130,34 @@ int attn_fwd_causal_bf16_ex(const void* q, const void* k, const void* v, void* o
 int attn_quantize_e4m3(const float* x, int64_t n, uint8_t* codes, float* descale, uint32_t* workspace,
                        void* stream);
 
+/* K smoothing for the quantisation pre-pass (paper Sec. V-E, "Rotation and K smoothing":
+ * the mean key of each head over the sequence is subtracted before the rotation).
+ * k: dense fp32 [B][S][H][D] (4-byte aligned), D in {128, 192}, S > 0;
+ * mean: [B][H][D] fp32, mean[b][h][d] = (1/S) sum_s k[b][s][h][d], summed in fp64 in a
+ * fixed order (chunks of 256 keys, then the chunks in sequence) and rounded once to fp32,
+ * so repeat calls give identical results and identical keys give their own value;
+ * workspace: attn_key_mean_workspace(B, S, H, D) bytes of device memory (8-byte
+ * aligned), overwritten.  B*H < 65536 and B*S*H*D < 2^31 (else ATTN_ERR_RANGE).
+ * B = 0 or H = 0 is a no-op. */
+int64_t attn_key_mean_workspace(int B, int S, int H, int D);
+int attn_key_mean(const float* k, int B, int S, int H, int D, float* mean, void* workspace, void* stream);
+
+/* Quantisation pre-pass with rotation (paper Sec. V-E, "Rotation and K smoothing", and
+ * Table XIII): y = (x - mean[b][h]) R with R = diag(signs) (C_m kron H_{D/m}), H the
+ * normalised Sylvester-Hadamard matrix, C_m the orthonormal DCT-II, m = 1 at D = 128 and
+ * 3 at D = 192 (element (a, b) -> (a', b') of the Kronecker product is C[a][a'] H[b][b'],
+ * index a*(D/m) + b), computed in fp32; then the per-tensor power-of-two e4m3 quantiser
+ * of attn_quantize_e4m3 with the scale taken from max |y|.  R is orthogonal, so
+ * (QR)(KR)^T = QK^T: rotate q and k with the same signs (k with its mean for K smoothing,
+ * q without), leave v unrotated, and call the attention entry points as usual.
+ * x: dense fp32 [B][S][H][D]; mean: [B][H][D] fp32, or NULL for no smoothing; signs: D
+ * fp32 values, each +1 or -1, drawn by the caller (other values do not give an orthogonal
+ * transform); codes: [B][S][H][D] bytes; descale and workspace as for attn_quantize_e4m3.
+ * B*S*H*D < 2^31.  y is computed twice (for the maximum, then for the codes) and never
+ * stored. */
+int attn_rotate_quantize_e4m3(const float* x, const float* mean, const float* signs, int B, int S, int H, int D,
+                              uint8_t* codes, float* descale, uint32_t* workspace, void* stream);
+
 /* fp32 -> bf16 rounding to nearest even (the BF16 operands of the paper's Sec. V-D
  * error measurement are the inputs rounded to BF16).  out: n uint16 bit patterns. */
 int attn_round_bf16(const float* x, int64_t n, uint16_t* out, void* stream);

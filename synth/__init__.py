@@ -123,14 +123,21 @@ def one_hot_key(B, S, H, dqk, dv, seed, key=0, lift=40.0):
     return q, k, v
 
 
-def activation_like(B, S, H, dqk, dv, seed, n_outlier=4, outlier_gain=20.0, sink_sigmas=12.0):
+def activation_sigma_raw(dqk, n_outlier=4, outlier_gain=20.0):
+    """Standard deviation of the raw non-sink dot products q.k of activation_like."""
+    return float(np.sqrt((dqk - n_outlier) + n_outlier * outlier_gain ** 4))
+
+
+def activation_like(B, S, H, dqk, dv, seed, n_outlier=4, outlier_gain=20.0, sink_sigmas=12.0, key_bias=0.0):
     """Activation-like input: q, k ~ N(0,1) with `n_outlier` seeded channels scaled by
     `outlier_gain` in both q and k, plus a sink key at position 0 whose dot product with
     every query equals `sink_sigmas` times the standard deviation of the raw non-sink
     dot products.  Construction: one further seeded channel c_s (not an outlier) is set
     to `outlier_gain` in every query; key 0 is zero except k[0, c_s] =
     sink_sigmas * sigma_raw / outlier_gain, with sigma_raw^2 = sum over channels of
-    E[q_ch^2] E[k_ch^2].  v ~ N(0, 1)."""
+    E[q_ch^2] E[k_ch^2].  v ~ N(0, 1).  key_bias > 0 adds one offset vector per (b, h),
+    ~ N(0, key_bias^2) per channel, to every key (a component shared by all keys of a
+    head, the part that K smoothing removes)."""
     rq, rk, rv, rs = _streams(seed)
     q = _normal(rq, (B, S, H, dqk))
     k = _normal(rk, (B, S, H, dqk))
@@ -145,6 +152,8 @@ def activation_like(B, S, H, dqk, dv, seed, n_outlier=4, outlier_gain=20.0, sink
     q[..., cs] = np.float32(outlier_gain)
     k[:, 0] = 0.0
     k[:, 0, :, cs] = np.float32(sink_sigmas * sigma_raw / outlier_gain)
+    if key_bias:
+        k += _normal(rs, (B, 1, H, dqk), key_bias)
     return q, k, v
 
 

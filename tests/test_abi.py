@@ -163,6 +163,27 @@ def test_prep_validation():
     assert L.attn_round_bf16(FAKE, 0, None, None) == 0
 
 
+def test_rotation_prepass_validation():
+    L = cfa.lib()
+    odd = ctypes.c_void_p((1 << 20) + 2)  # not 4-byte aligned
+    assert L.attn_key_mean_workspace(2, 300, 3, 128) == 2 * 3 * 2 * 128 * 8  # two chunks of 256 keys, fp64
+    assert L.attn_key_mean_workspace(1, 256, 1, 64) == -2
+    assert L.attn_key_mean(FAKE, 1, 256, 1, 96, FAKE, FAKE, None) == -2
+    assert L.attn_key_mean(FAKE, 1, 0, 1, 128, FAKE, FAKE, None) == -2
+    assert L.attn_key_mean(None, 0, 256, 1, 128, None, None, None) == 0
+    assert L.attn_key_mean(None, 1, 256, 1, 128, FAKE, FAKE, None) == -1
+    assert L.attn_key_mean(odd, 1, 256, 1, 128, FAKE, FAKE, None) == -3
+    assert L.attn_key_mean(FAKE, 1, 256, 1, 128, FAKE, ctypes.c_void_p((1 << 20) + 4), None) == -3
+    assert L.attn_key_mean(FAKE, 1 << 14, 256, 8, 128, FAKE, FAKE, None) == -4
+    rq = L.attn_rotate_quantize_e4m3
+    assert rq(FAKE, None, FAKE, 1, 256, 1, 64, FAKE, FAKE, FAKE, None) == -2
+    assert rq(FAKE, None, FAKE, -1, 256, 1, 128, FAKE, FAKE, FAKE, None) == -2
+    assert rq(FAKE, None, None, 1, 256, 1, 128, FAKE, FAKE, FAKE, None) == -1
+    assert rq(None, None, FAKE, 1, 256, 1, 128, FAKE, FAKE, FAKE, None) == -1
+    assert rq(FAKE, odd, FAKE, 1, 256, 1, 192, FAKE, FAKE, FAKE, None) == -3
+    assert rq(FAKE, None, FAKE, 1 << 10, 1 << 12, 8, 128, FAKE, FAKE, FAKE, None) == -4
+
+
 def test_status_strings():
     L = cfa.lib()
     for c in range(-7, 1):
