@@ -15,6 +15,7 @@ Pins (what ties each function to something other than itself) live in
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 from dataclasses import dataclass
@@ -132,6 +133,24 @@ def quantize_e4m3_f64(x: np.ndarray):
     return codes, float(ds)
 
 
+def static_exponent(descale: float) -> int:
+    """k with descale = 2^-k, for a power-of-two descale in [2^-126, 2^126]."""
+    m, e = math.frexp(float(descale))
+    if m != 0.5 or not -126 <= 1 - e <= 126:
+        raise ValueError(f"descale {descale!r} is not a power of two in [2^-126, 2^126]")
+    return 1 - e
+
+
+def quantize_e4m3_static(x: np.ndarray, descale: float) -> np.ndarray:
+    """The quantiser with a given (static) power-of-two descale instead of one from the
+    tensor's maximum (paper Sec. V-E: the fused quantisation pass uses a static scale
+    set from calibration, footnote 17 on power-of-two descales): codes are
+    e4m3_rne(x / descale), so scaled values beyond 448 saturate to +-448."""
+    k = static_exponent(descale)
+    x = np.asarray(x, dtype=np.float64)
+    return e4m3_rne(np.ldexp(x, k)).reshape(x.shape)
+
+
 # ----------------------------------------------------------------------------- rotation
 # Paper Sec. V-E, "Rotation and K smoothing": after RoPE, Q and K are multiplied by the
 # same orthogonal R = diag(s) (C_m kron H_{D/m}), s random signs, H the normalised
@@ -185,6 +204,11 @@ def rotate(x: np.ndarray, signs, mean: np.ndarray = None) -> np.ndarray:
 def rotate_quantize_e4m3(x: np.ndarray, signs, mean: np.ndarray = None):
     """Rotation (and optional K smoothing) in fp64, then the per-tensor quantiser."""
     return quantize_e4m3_f64(rotate(x, signs, mean))
+
+
+def rotate_quantize_e4m3_static(x: np.ndarray, signs, descale: float, mean: np.ndarray = None) -> np.ndarray:
+    """Rotation (and optional K smoothing) in fp64, then the static-scale quantiser."""
+    return quantize_e4m3_static(rotate(x, signs, mean), descale)
 
 
 def leanp_code(x: float, sigma: int = SIGMA, beta: float = BETA) -> int:

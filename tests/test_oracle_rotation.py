@@ -123,3 +123,35 @@ def test_rotation_lowers_input_error_with_outlier_channels(orc, D):
 
     e0, e1 = score_err(q, k, False), score_err(q, k, True)
     assert e1 < 0.75 * e0, (e0, e1)
+
+
+def test_static_quantiser_equals_per_call_at_its_descale(orc):
+    """With the descale the per-call rule picks, the static quantiser gives the same codes
+    (fp32 and fp64 inputs, plain and rotated)."""
+    rng = np.random.default_rng(12)
+    x = (rng.standard_normal((1, 64, 2, 128)) * 5).astype(np.float32)
+    c, d = orc.quantize_e4m3(x)
+    assert np.array_equal(orc.quantize_e4m3_static(x, d), c)
+    s = _signs(128, 2)
+    c2, d2 = orc.rotate_quantize_e4m3(x, s, orc.key_mean(x))
+    assert np.array_equal(orc.rotate_quantize_e4m3_static(x, s, d2, orc.key_mean(x)), c2)
+    # a larger descale (coarser codes) halves every value before rounding: codes of x/2
+    assert np.array_equal(orc.quantize_e4m3_static(x, 2 * d), c_half := orc.quantize_e4m3_static(x / 2, d))
+    assert c_half.shape == x.shape
+
+
+def test_static_quantiser_saturates(orc):
+    t = orc.e4m3_table()
+    x = np.array([1000.0, -1000.0, 448.0, 449.0, 463.9, 464.0, 480.0, -3e38, 0.5, -0.0])
+    got = t[orc.quantize_e4m3_static(x, 1.0)]
+    assert np.array_equal(got[:8], [448, -448, 448, 448, 448, 448, 448, -448])
+    assert got[8] == 0.5 and got[9] == 0.0
+    # descale 2^-3: x / descale = 8 x, so |x| > 56 saturates
+    y = np.array([56.0, 57.0, -200.0, 0.125])
+    assert np.array_equal(t[orc.quantize_e4m3_static(y, 0.125)] * 0.125, [56.0, 56.0, -56.0, 0.125])
+
+
+@pytest.mark.parametrize("bad", [0.0, 3.0, 0.75, -0.5, 2.0 ** 127, 2.0 ** -127, float("inf"), float("nan")])
+def test_static_descale_must_be_power_of_two(orc, bad):
+    with pytest.raises(ValueError):
+        orc.quantize_e4m3_static(np.ones(4), bad)
