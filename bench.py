@@ -232,11 +232,12 @@ def run_bf16(torch, cfa, B, H, S, warmup, steps, seed=0, sustained=False, dqk=12
 
 
 def run_rotate_prepass(torch, cfa, B, H, S, D, warmup, steps, seed=0):
-    """Input preparation with rotation and K smoothing (q, k rotated; k smoothed; v plain)
-    against plain per-tensor quantisation of q, k, v, both on fp32 inputs in HBM.
-    Algorithmic bytes per element: the key mean reads k once (4); each quantiser reads its
-    tensor twice (the per-tensor scale needs max |y| before the first code) and writes
-    one byte (9)."""
+    """Input preparation of q, k, v from fp32 in HBM, four ways: per-call scales (each
+    quantiser reads its tensor twice, since the scale needs max |y| before the first
+    code) or static power-of-two scales (one pass, the paper's fused quantisation pass),
+    each plain or with the rotation of q and k and K smoothing (the key mean reads k once
+    more).  Algorithmic bytes per element of each tensor: 9 per-call, 5 static, +4 for the
+    key mean."""
     import synth
     q, k, v = synth.gaussian(B, S, H, D, D, seed)
     dev = torch.device("cuda:0")
@@ -244,23 +245,43 @@ def run_rotate_prepass(torch, cfa, B, H, S, D, warmup, steps, seed=0):
     del q, k, v
     sg = torch.from_numpy(np.where(np.random.default_rng(seed).integers(0, 2, D) == 1, 1.0, -1.0)
                           .astype(np.float32)).to(dev)
+    mean = cfa.key_mean(kg)
+    ds = [float(cfa.rotate_quantize_e4m3(qg, sg)[1].item()), float(cfa.rotate_quantize_e4m3(kg, sg, mean)[1].item()),
+          float(cfa.quantize_e4m3(vg)[1].item())]
+    dp = [float(cfa.quantize_e4m3(t)[1].item()) for t in (qg, kg)]
 
-    def rotated():
+    def call_rot():
         cfa.rotate_quantize_e4m3(qg, sg)
         cfa.rotate_quantize_e4m3(kg, sg, cfa.key_mean(kg))
         cfa.quantize_e4m3(vg)
 
-    def plain():
+    def call_plain():
         for t in (qg, kg, vg):
             cfa.quantize_e4m3(t)
 
+    def static_rot():
+        cfa.rotate_quantize_e4m3_static(qg, sg, ds[0])
+        cfa.rotate_quantize_e4m3_static(kg, sg, ds[1], cfa.key_mean(kg))
+        cfa.quantize_e4m3_static(vg, ds[2])
+
+    def static_rot_nosmooth():
+        cfa.rotate_quantize_e4m3_static(qg, sg, ds[0])
+        cfa.rotate_quantize_e4m3_static(kg, sg, ds[1])
+        cfa.quantize_e4m3_static(vg, ds[2])
+
+    def static_plain():
+        for t, d in zip((qg, kg, vg), dp + [ds[2]]):
+            cfa.quantize_e4m3_static(t, d)
+
     n = B * S * H * D
-    ms_r = time_launches(torch, rotated, warmup, steps)
-    ms_p = time_launches(torch, plain, warmup, steps)
+    out = {}
+    for name, fn, nbytes in (("per_call_rotated_smoothed", call_rot, 31 * n), ("per_call_plain", call_plain, 27 * n),
+                             ("static_rotated_smoothed", static_rot, 19 * n),
+                             ("static_rotated", static_rot_nosmooth, 15 * n), ("static_plain", static_plain, 15 * n)):
+        ms = time_launches(torch, fn, warmup, steps)
+        out[name] = {"ms": round(ms, 4), "hbm_gbs_at_algorithmic_bytes": round(nbytes / (ms * 1e-3) / 1e9, 1)}
     del qg, kg, vg
-    return {"ms": round(ms_r, 4), "ms_plain_quantise": round(ms_p, 4),
-            "hbm_gbs_at_algorithmic_bytes": round(31 * n / (ms_r * 1e-3) / 1e9, 1),
-            "plain_hbm_gbs_at_algorithmic_bytes": round(27 * n / (ms_p * 1e-3) / 1e9, 1)}
+    return out
 
 
 def cpu_baseline(B, H, S, dqk, budget_s=20.0, seed=0):

@@ -13,6 +13,7 @@ Functions mirror the C entry points:
     attn_fwd_causal_bf16_ex(q, k, v, softmax_scale=None)
     quantize_e4m3(x) -> (codes, descale)      round_bf16(x) -> bf16 tensor
     key_mean(k) -> mean [B, H, D]             rotate_quantize_e4m3(x, signs, mean=None) -> (codes, descale)
+    quantize_e4m3_static(x, descale) -> codes rotate_quantize_e4m3_static(x, signs, descale, mean=None) -> codes
 Tensors are BSHD: q, k [B, S, H, d_qk], v [B, S, H, d_v]; outputs out [B, S, H, d_v]
 (bfloat16) and lse [B, H, S] (float32).  The *_ex functions take BSHD-shaped views of any
 strided layout (e.g. a BHSD tensor x passed as x.permute(0, 2, 1, 3)) with the head
@@ -71,6 +72,8 @@ def lib():
         L.attn_key_mean_workspace.restype = I64
         L.attn_key_mean.argtypes = [P, I, I, I, I, P, P, P]
         L.attn_rotate_quantize_e4m3.argtypes = [P, P, P, I, I, I, I, P, P, P, P]
+        L.attn_quantize_e4m3_static.argtypes = [P, I64, F, P, P]
+        L.attn_rotate_quantize_e4m3_static.argtypes = [P, P, P, I, I, I, I, F, P, P]
         L.attn_default_grid.argtypes = [I, I, I, I]
         L.attn_schedule.argtypes = [I, I, I, I, P, I64]
         L.attn_schedule.restype = I64
@@ -79,7 +82,7 @@ def lib():
         for name in ("attn_fwd_causal_fp8", "attn_fwd_causal_mla", "attn_fwd_causal_fp8_debug",
                      "attn_fwd_causal_bf16", "attn_fwd_causal_fp8_ex", "attn_fwd_causal_bf16_ex",
                      "attn_quantize_e4m3", "attn_round_bf16", "attn_default_grid", "attn_key_mean",
-                     "attn_rotate_quantize_e4m3"):
+                     "attn_rotate_quantize_e4m3", "attn_quantize_e4m3_static", "attn_rotate_quantize_e4m3_static"):
             getattr(L, name).restype = I
         _lib = L
     return _lib
@@ -272,17 +275,44 @@ def key_mean(k):
     return mean
 
 
-def rotate_quantize_e4m3(x, signs, mean=None, workspace=None):
-    """Rotate rows of x [B, S, H, D] by diag(signs) (C_m kron H_{D/m}) after subtracting
-    mean [B, H, D] (if given), then quantise to e4m3 with one power-of-two scale.
-
-    Returns (codes as float8_e4m3fn with x's shape, descale as a 1-element float32 tensor)."""
+def _rot_checks(x, signs, mean):
     B, S, H, D = _bshd_f32(x, "x")
     if signs.dtype != torch.float32 or not signs.is_cuda or signs.shape != (D,) or not signs.is_contiguous():
         raise TypeError("signs must be a contiguous float32 GPU tensor of D values")
     if mean is not None and (mean.dtype != torch.float32 or not mean.is_cuda or mean.shape != (B, H, D)
                              or not mean.is_contiguous()):
         raise TypeError("mean must be a contiguous float32 GPU tensor [B, H, D]")
+    return B, S, H, D
+
+
+def quantize_e4m3_static(x, descale):
+    """e4m3 codes of x / descale for a given power-of-two descale (static scale); scaled
+    values beyond 448 saturate.  Returns codes as float8_e4m3fn with x's shape."""
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise TypeError("x must be a contiguous float32 GPU tensor")
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    rc = lib().attn_quantize_e4m3_static(_ptr(x), x.numel(), float(descale), _ptr(codes), _stream())
+    _check("attn_quantize_e4m3_static", rc)
+    return codes.view(torch.float8_e4m3fn)
+
+
+def rotate_quantize_e4m3_static(x, signs, descale, mean=None):
+    """The rotation of rotate_quantize_e4m3 followed by the static-scale quantiser (one
+    pass over x).  Returns codes as float8_e4m3fn with x's shape."""
+    B, S, H, D = _rot_checks(x, signs, mean)
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    rc = lib().attn_rotate_quantize_e4m3_static(_ptr(x), _ptr(mean), _ptr(signs), B, S, H, D, float(descale),
+                                                _ptr(codes), _stream())
+    _check("attn_rotate_quantize_e4m3_static", rc)
+    return codes.view(torch.float8_e4m3fn)
+
+
+def rotate_quantize_e4m3(x, signs, mean=None, workspace=None):
+    """Rotate rows of x [B, S, H, D] by diag(signs) (C_m kron H_{D/m}) after subtracting
+    mean [B, H, D] (if given), then quantise to e4m3 with one power-of-two scale.
+
+    Returns (codes as float8_e4m3fn with x's shape, descale as a 1-element float32 tensor)."""
+    B, S, H, D = _rot_checks(x, signs, mean)
     codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     descale = torch.empty(1, dtype=torch.float32, device=x.device)
     if workspace is None:

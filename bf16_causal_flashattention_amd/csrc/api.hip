@@ -186,6 +186,32 @@ int run_bf16(const Problem& p, float sm, void* stream) {
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
+// Power-of-two descale in [2^-126, 2^126] -> the scale 2^k that multiplies x; 0 if invalid.
+float static_scale_of(float descale) {
+  int e;
+  const float m = frexpf(descale, &e);  // descale = m 2^e; a power of two has m = 0.5
+  if (!(m == 0.5f) || e - 1 < -126 || e - 1 > 126) return 0.f;
+  return ldexpf(1.f, 1 - e);
+}
+
+int check_rotate(const float* x, const float* mean, const float* signs, int B, int S, int H, int D,
+                 const uint8_t* codes) {
+  if (B < 0 || S < 0 || H < 0 || (D != 128 && D != 192)) return ATTN_ERR_SHAPE;
+  if (!signs) return ATTN_ERR_NULL;
+  const int64_t n = (int64_t)B * S * H * D;
+  if (n > 0 && (!x || !codes)) return ATTN_ERR_NULL;
+  if (!aligned(x, 4) || !aligned(signs, 4) || !aligned(mean, 4)) return ATTN_ERR_ALIGN;
+  if (n >= (INT64_C(1) << 31)) return ATTN_ERR_RANGE;
+  return ATTN_OK;
+}
+
+// orthonormal DCT-II of size 3 (the C_m factor at D = 192): C[k][n] = a_k cos(pi (2n+1) k / 6)
+void dct3(float c3[9]) {
+  for (int kk = 0; kk < 3; ++kk)
+    for (int nn = 0; nn < 3; ++nn)
+      c3[3 * kk + nn] = (float)((kk == 0 ? sqrt(1.0 / 3.0) : sqrt(2.0 / 3.0)) * cos(M_PI * (2 * nn + 1) * kk / 6.0));
+}
+
 }  // namespace
 
 extern "C" {
@@ -270,20 +296,39 @@ int attn_key_mean(const float* k, int B, int S, int H, int D, float* mean, void*
 
 int attn_rotate_quantize_e4m3(const float* x, const float* mean, const float* signs, int B, int S, int H, int D,
                               uint8_t* codes, float* descale, uint32_t* workspace, void* stream) {
-  if (B < 0 || S < 0 || H < 0 || (D != 128 && D != 192)) return ATTN_ERR_SHAPE;
-  if (!descale || !workspace || !signs) return ATTN_ERR_NULL;
-  const int64_t n = (int64_t)B * S * H * D;
-  if (n > 0 && (!x || !codes)) return ATTN_ERR_NULL;
-  if (!aligned(x, 4) || !aligned(signs, 4) || !aligned(mean, 4) || !aligned(descale, 4) || !aligned(workspace, 4))
-    return ATTN_ERR_ALIGN;
-  if (n >= (INT64_C(1) << 31)) return ATTN_ERR_RANGE;
-  // orthonormal DCT-II of size 3 (the C_m factor at D = 192): C[k][n] = a_k cos(pi (2n+1) k / 6)
+  const int rc = check_rotate(x, mean, signs, B, S, H, D, codes);
+  if (rc != ATTN_OK) return rc;
+  if (!descale || !workspace) return ATTN_ERR_NULL;
+  if (!aligned(descale, 4) || !aligned(workspace, 4)) return ATTN_ERR_ALIGN;
   float c3[9];
-  for (int kk = 0; kk < 3; ++kk)
-    for (int nn = 0; nn < 3; ++nn)
-      c3[3 * kk + nn] = (float)((kk == 0 ? sqrt(1.0 / 3.0) : sqrt(2.0 / 3.0)) * cos(M_PI * (2 * nn + 1) * kk / 6.0));
-  const hipError_t e = cfa::launch_rotate_quantize(x, mean, signs, B, S, H, D, c3, codes, descale, workspace,
-                                                   (hipStream_t)stream);
+  dct3(c3);
+  const hipError_t e = cfa::launch_rotate_quantize(x, mean, signs, B, S, H, D, c3, codes, descale, workspace, 1.f,
+                                                   false, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int attn_rotate_quantize_e4m3_static(const float* x, const float* mean, const float* signs, int B, int S, int H,
+                                     int D, float descale, uint8_t* codes, void* stream) {
+  const int rc = check_rotate(x, mean, signs, B, S, H, D, codes);
+  if (rc != ATTN_OK) return rc;
+  const float scale = static_scale_of(descale);
+  if (scale == 0.f) return ATTN_ERR_ARG;
+  if ((int64_t)B * S * H == 0) return ATTN_OK;
+  float c3[9];
+  dct3(c3);
+  const hipError_t e = cfa::launch_rotate_quantize(x, mean, signs, B, S, H, D, c3, codes, nullptr, nullptr, scale,
+                                                   true, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int attn_quantize_e4m3_static(const float* x, int64_t n, float descale, uint8_t* codes, void* stream) {
+  if (n < 0) return ATTN_ERR_ARG;
+  const float scale = static_scale_of(descale);
+  if (scale == 0.f) return ATTN_ERR_ARG;
+  if (n == 0) return ATTN_OK;
+  if (!x || !codes) return ATTN_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(codes, 4)) return ATTN_ERR_ALIGN;
+  const hipError_t e = cfa::launch_quantize_e4m3_static(x, n, scale, codes, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

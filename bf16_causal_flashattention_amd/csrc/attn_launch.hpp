@@ -47,8 +47,11 @@ hipError_t launch_quantize_e4m3(const float* x, int64_t n, uint8_t* codes, float
 hipError_t launch_round_bf16(const float* x, int64_t n, uint16_t* out, hipStream_t stream);
 int64_t key_mean_workspace_bytes(int B, int S, int H, int D);
 hipError_t launch_key_mean(const float* k, int B, int S, int H, int D, float* mean, void* ws, hipStream_t stream);
+// static_scale / is_static: one pass with the given power-of-two scale (saturating at 448)
+// instead of the two-pass maximum-derived scale (descale and ws unused then).
 hipError_t launch_rotate_quantize(const float* x, const float* mean, const float* signs, int B, int S, int H,
                                   int D, const float c3[9], uint8_t* codes, float* descale, uint32_t* ws,
-                                  hipStream_t stream);
+                                  float static_scale, bool is_static, hipStream_t stream);
+hipError_t launch_quantize_e4m3_static(const float* x, int64_t n, float scale, uint8_t* codes, hipStream_t stream);
 
 }  // namespace cfa

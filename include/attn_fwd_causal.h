@@ -134,7 +134,7 @@ int attn_quantize_e4m3(const float* x, int64_t n, uint8_t* codes, float* descale
  * the mean key of each head over the sequence is subtracted before the rotation).
  * k: dense fp32 [B][S][H][D] (4-byte aligned), D in {128, 192}, S > 0;
  * mean: [B][H][D] fp32, mean[b][h][d] = (1/S) sum_s k[b][s][h][d], summed in fp64 in a
- * fixed order (chunks of 256 keys, then the chunks in sequence) and rounded once to fp32,
+ * fixed order (chunks of 1024 keys, then the chunks in sequence) and rounded once to fp32,
  * so repeat calls give identical results and identical keys give their own value;
  * workspace: attn_key_mean_workspace(B, S, H, D) bytes of device memory (8-byte
  * aligned), overwritten.  B*H < 65536 and B*S*H*D < 2^31 (else ATTN_ERR_RANGE).
@@ -157,6 +157,17 @@ int attn_key_mean(const float* k, int B, int S, int H, int D, float* mean, void*
  * stored. */
 int attn_rotate_quantize_e4m3(const float* x, const float* mean, const float* signs, int B, int S, int H, int D,
                               uint8_t* codes, float* descale, uint32_t* workspace, void* stream);
+
+/* Static-scale quantisers (paper Sec. V-E: the fused quantisation pass uses a static
+ * power-of-two scale, set per tensor from calibration, so it needs no pass for the
+ * maximum).  descale: a host float, a power of two in [2^-126, 2^126] (else ATTN_ERR_ARG);
+ * codes[i] = e4m3_rne(x[i] / descale), and scaled values beyond +-448 saturate to +-448.
+ * attn_quantize_e4m3_static: n fp32 values (x 16-byte aligned, codes 4-byte aligned).
+ * attn_rotate_quantize_e4m3_static: the rotation of attn_rotate_quantize_e4m3 (same
+ * arguments and layout) followed by this quantiser; one read of x, one write of codes. */
+int attn_quantize_e4m3_static(const float* x, int64_t n, float descale, uint8_t* codes, void* stream);
+int attn_rotate_quantize_e4m3_static(const float* x, const float* mean, const float* signs, int B, int S, int H,
+                                     int D, float descale, uint8_t* codes, void* stream);
 
 /* fp32 -> bf16 rounding to nearest even (the BF16 operands of the paper's Sec. V-D
  * error measurement are the inputs rounded to BF16).  out: n uint16 bit patterns. */

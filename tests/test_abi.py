@@ -166,7 +166,7 @@ def test_prep_validation():
 def test_rotation_prepass_validation():
     L = cfa.lib()
     odd = ctypes.c_void_p((1 << 20) + 2)  # not 4-byte aligned
-    assert L.attn_key_mean_workspace(2, 300, 3, 128) == 2 * 3 * 2 * 128 * 8  # two chunks of 256 keys, fp64
+    assert L.attn_key_mean_workspace(2, 1500, 3, 128) == 2 * 3 * 2 * 128 * 8  # two chunks of 1024 keys, fp64
     assert L.attn_key_mean_workspace(1, 256, 1, 64) == -2
     assert L.attn_key_mean(FAKE, 1, 256, 1, 96, FAKE, FAKE, None) == -2
     assert L.attn_key_mean(FAKE, 1, 0, 1, 128, FAKE, FAKE, None) == -2
@@ -182,6 +182,17 @@ def test_rotation_prepass_validation():
     assert rq(None, None, FAKE, 1, 256, 1, 128, FAKE, FAKE, FAKE, None) == -1
     assert rq(FAKE, odd, FAKE, 1, 256, 1, 192, FAKE, FAKE, FAKE, None) == -3
     assert rq(FAKE, None, FAKE, 1 << 10, 1 << 12, 8, 128, FAKE, FAKE, FAKE, None) == -4
+    rs = L.attn_rotate_quantize_e4m3_static
+    for bad in (0.0, 3.0, -0.5, 2.0 ** 127, 2.0 ** -127, float("inf"), float("nan")):
+        assert rs(FAKE, None, FAKE, 1, 256, 1, 128, bad, FAKE, None) == -5, bad
+        assert L.attn_quantize_e4m3_static(FAKE, 16, bad, FAKE, None) == -5, bad
+    assert rs(FAKE, None, FAKE, 1, 256, 1, 96, 1.0, FAKE, None) == -2
+    assert rs(FAKE, None, None, 1, 256, 1, 128, 1.0, FAKE, None) == -1
+    assert rs(FAKE, None, FAKE, 1, 256, 1, 128, 1.0, None, None) == -1
+    assert rs(None, None, FAKE, 0, 256, 1, 128, 2.0 ** -126, None, None) == 0
+    assert L.attn_quantize_e4m3_static(MISALIGNED, 16, 1.0, FAKE, None) == -3
+    assert L.attn_quantize_e4m3_static(FAKE, -1, 1.0, FAKE, None) == -5
+    assert L.attn_quantize_e4m3_static(None, 0, 2.0 ** 126, None, None) == 0
 
 
 def test_status_strings():

@@ -63,10 +63,14 @@ def test_key_mean_identical_keys_exact():
     assert np.array_equal(g, k[:, 0])
 
 
-def _check_codes(codes_g, ds_g, x, signs, mean64):
-    """GPU codes against the oracle's fp64 rotation + quantiser."""
+def _check_codes(codes_g, ds_g, x, signs, mean64, static=False):
+    """GPU codes against the oracle's fp64 rotation + quantiser (per-call scale, or the
+    static descale ds_g)."""
     y = oracle.rotate(x, signs, mean64)
-    oc, od = oracle.quantize_e4m3_f64(y)
+    if static:
+        oc, od = oracle.quantize_e4m3_static(y, ds_g), ds_g
+    else:
+        oc, od = oracle.quantize_e4m3_f64(y)
     assert ds_g == od, (ds_g, od)
     g = codes_g.view(torch.uint8).cpu().numpy()
     diff = g != oc
@@ -87,10 +91,13 @@ def _check_codes(codes_g, ds_g, x, signs, mean64):
     return g
 
 
-@pytest.mark.parametrize("B,S,H,D,smooth", [(2, 300, 3, 128, True), (2, 300, 3, 192, True),
+@pytest.mark.parametrize("B,S,H,D,smooth", [(2, 301, 3, 128, True), (2, 303, 3, 192, True),
                                             (1, 512, 2, 128, False), (1, 777, 2, 192, False),
-                                            (1, 4096, 8, 128, True), (1, 2048, 4, 192, True)])
+                                            (1, 4096, 8, 128, True), (1, 2048, 4, 192, True),
+                                            (1, 42, 2050, 128, True)])
 def test_rotate_quantize(B, S, H, D, smooth):
+    """S not a multiple of the 4 positions a wave takes at a time; more than 2048 heads
+    (waves move from head to head and reload the mean)."""
     _case("rotate_quantize", B, S, H, D, smooth)
     q, k, _ = _inputs(B, S, H, D, 5 * S + D + smooth)
     s = _signs(D, S + D)
@@ -102,6 +109,42 @@ def test_rotate_quantize(B, S, H, D, smooth):
         torch.cuda.synchronize()
         print("tensor", name, flush=True)
         _check_codes(codes, float(ds.item()), x, s, oracle.key_mean(x) if smooth else None)
+
+
+@pytest.mark.parametrize("B,S,H,D,smooth", [(2, 300, 3, 128, True), (1, 777, 2, 192, False),
+                                            (1, 2048, 4, 192, True)])
+def test_rotate_quantize_static(B, S, H, D, smooth):
+    """The one-pass static-scale form: at the per-call descale it must give the per-call
+    codes bit for bit (same transform, same rounding); at a quarter of it the largest
+    values saturate, checked against the oracle's static quantiser."""
+    _case("rotate_quantize_static", B, S, H, D, smooth)
+    _, k, _ = _inputs(B, S, H, D, 9 * S + D)
+    s = _signs(D, 2 * S + D)
+    sg, kg = _dev(s), _dev(k)
+    mg = cfa.key_mean(kg) if smooth else None
+    c_call, d_call = cfa.rotate_quantize_e4m3(kg, sg, mg)
+    d_call = float(d_call.item())
+    c_static = cfa.rotate_quantize_e4m3_static(kg, sg, d_call, mg)
+    c_sat = cfa.rotate_quantize_e4m3_static(kg, sg, d_call / 4, mg)
+    torch.cuda.synchronize()
+    assert torch.equal(c_call.view(torch.uint8), c_static.view(torch.uint8))
+    g = _check_codes(c_sat, d_call / 4, k, s, oracle.key_mean(k) if smooth else None, static=True)
+    n_sat = int(np.sum((g & 0x7F) == 0x7E))
+    print("RESULT", {"saturated": n_sat}, flush=True)
+    assert n_sat > 0
+
+
+@pytest.mark.parametrize("n", [4096 * 33, 1001])
+def test_quantize_static(n):
+    """Plain static-scale quantiser: bit-exact against the oracle (the scaling by a power of
+    two is exact, the rounding is RNE), with and without saturation, ragged n."""
+    _case("quantize_static", n)
+    x = (np.random.default_rng(n).standard_normal(n) * 3).astype(np.float32)
+    _, d = oracle.quantize_e4m3(x)
+    xg = _dev(x)
+    for ds in (d, d / 8, d * 2):
+        got = cfa.quantize_e4m3_static(xg, ds).view(torch.uint8).cpu().numpy()
+        assert np.array_equal(got, oracle.quantize_e4m3_static(x, ds)), ds
 
 
 def test_rotate_quantize_degenerate():
