@@ -13,10 +13,15 @@
 //   Sec. VI-A  the softmax scale multiplies the fp32 scores (not folded into bf16 Q).
 //
 // Schedule and barrier placement follow the FP8 kernel (attn_fp8.hip): group 1 (waves 4-7)
-// runs one phase behind group 0; M_i issues O += V(i)^T P(i) and S(i+1) = K(i+1) Q^T (MFMAs
-// and their operand reads only, each operand read three MFMAs ahead, consecutive MFMAs on
-// different accumulators); S_i takes the next block's maximum, the lazy decision (with the
-// rare rescale of O and l) and forms P(i+1).  K and V blocks move by DMA issued at the end
+// runs one phase behind group 0; M_i issues O += V(i)^T P(i) and S(i+1) = K(i+1) Q^T as one
+// stream of MFMAs and their operand reads (each operand read three MFMAs ahead through a
+// ring of registers, consecutive MFMAs on different accumulators, the K reads of the QK
+// part issued behind the last PV MFMAs); the first three V operands of M_i are read at the
+// end of S_{i-1}, after its wait for the copies (V(i) has been in LDS since the phase
+// before), so the matrix phase starts with its operands in registers.  On a wave's last
+// live block the QK part still runs, on the other K slot (in-bounds LDS, scores unused),
+// which keeps one shape of the stream.  S_i takes the next block's maximum, the lazy
+// decision (with the rare rescale of O and l) and forms P(i+1).  K and V blocks move by DMA issued at the end
 // of M_i, after the phase's last operand read: group 0 copies K(i+2) into the slot of
 // K(i) (two K slots), group 1 copies V(i+2) into the slot of V(i-1) (three V slots); each
 // wave waits for its copies at the end of S_i.  Every target slot was last read in an
@@ -247,34 +252,55 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
           for (int e = 0; e < 4; ++e) pb[mm][e] = (int)cvt_pk_bf16(p[2 * e], p[2 * e + 1]);
         }
       };
-      // O^T += V^T P^T.  The four d tiles alternate (independent accumulators); each
-      // MFMA's operand (two transpose reads) is read one MFMA ahead.
-      auto pv = [&](int blk) {
-        const uint8_t* sv = smem + (blk % 3) * kVSlot + v_tr;
-        // lane: d = 32dt + l32, bf16 of keys 16mm + 8hh + 0..7
-        auto vread = [&](int t) {
+      // Operand stream of a matrix phase: the 16 PV MFMAs (O^T += V^T P^T) of block blk, then
+      // the 2 QM QK MFMAs of block blk+1.  Operand t is read kDist MFMAs ahead of its MFMA
+      // through the ring opb; the first kDist (V operands) are read by preload().
+      constexpr int kDist = 3;
+      constexpr int NQ = 2 * QM;
+      v4i opb[kDist + 1];
+      // lane: V^T operand d = 32dt + l32 over keys 16mm + 8hh + 0..7 (two transpose reads);
+      // K operand as in qk()
+      auto opread = [&](int blk, int t) -> v4i {
+        if (t < 16) {
+          const uint8_t* sv = smem + (blk % 3) * kVSlot + v_tr;
           const int dt = t & 3, mm = t >> 2;
           const v2i r0 = lds_tr16(sv + (16 * mm) * kVStride + 64 * dt);
           const v2i r1 = lds_tr16(sv + (16 * mm + 4) * kVStride + 64 * dt);
           return (v4i){r0[0], r0[1], r1[0], r1[1]};
-        };
-        constexpr int D = 3;
-        v4i vop[D + 1];
-#pragma unroll
-        for (int t = 0; t < D; ++t) vop[t] = vread(t);
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          const int dt = t & 3, mm = t >> 2;
-          if (t + D < 16) vop[(t + D) % (D + 1)] = vread(t + D);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(vop[t % (D + 1)]), as_bf(pb[mm]), oacc[dt], 0, 0, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * D, 1);
+        const int tq = t - 16;
+        const uint8_t* sk = smem + ((blk + 1) & 1) * kKSlot + k_rd;
+        return *(const v4i*)(sk + 32 * (tq & 1) * kKStride + 32 * (tq >> 1));
+      };
+      auto preload = [&](int blk) {
 #pragma unroll
-        for (int t = 0; t < 16 - D; ++t) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        for (int t = 0; t < kDist; ++t) opb[t] = opread(blk, t);
+      };
+      auto stream = [&](int blk) {
+        constexpr int N = 16 + NQ;
+#pragma unroll
+        for (int t = 0; t < N; ++t) {
+          if (t + kDist < N) opb[(t + kDist) % (kDist + 1)] = opread(blk, t + kDist);
+          const v4i op = opb[t % (kDist + 1)];
+          if (t < 16) {
+            const int dt = t & 3, mm = t >> 2;
+            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(op), as_bf(pb[mm]), oacc[dt], 0, 0, 0);
+          } else {
+            const int tq = t - 16, u = tq & 1, mm = tq >> 1;
+            sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(op), as_bf(qop[mm]), mm == 0 ? zero16 : sacc[u],
+                                                              0, 0, 0);
+          }
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, D, 1);
+        // issue order: each MFMA, then the reads of the operand kDist MFMAs ahead of it
+#pragma unroll
+        for (int t = 0; t < N; ++t) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          const int nr = t + kDist < N ? (t + kDist < 16 ? 2 : 1) : 0;
+          if (nr == 2)
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          else if (nr == 1)
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
       };
 
       stage(0);
@@ -288,6 +314,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
       if (live(0)) {
         max_step(0, true);
         probs();
+        preload(0);
       }
       lds_barrier();
 
@@ -295,8 +322,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
         // -------------------------------------------------------------- M_i
         __builtin_amdgcn_s_setprio(1);
         const bool live_i = live(i), live_n = (i + 1 < nb) && live(i + 1);
-        if (live_i) pv(i);
-        if (live_n) qk(i + 1);
+        if (live_i) stream(i);
         // after this phase's last operand read: K(i+2) by group 0 into the slot of K(i),
         // V(i+2) by group 1 into the slot of V(i-1); waited for at the end of S_i
         if (i + 2 < nb) stage(i + 2);
@@ -308,6 +334,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
           probs();
         }
         if (i + 2 < nb) wait_dma();
+        if (live_n) preload(i + 1);  // V(i+1): its copy was waited for at least one phase ago
         lds_barrier();
       }
       if (grp == 0) lds_barrier();
