@@ -107,3 +107,75 @@ def test_c3_bf16_b1_h32_sweep(S):
     assert res["fp64_rms"] <= TOL_FP64_RMS_BF16 and res["lse_fp64"] <= 1e-3
     del out, lse, gq, gk, gv
     torch.cuda.empty_cache()
+
+
+def _fp8_ex_full(B, H, Hkv, S, dqk, p_mode, exact_p, seed, n_groups):
+    """The general entry point at a bench.py size: q with H heads, k/v with Hkv heads (inputs
+    as bench.py makes them); the oracle sees k/v expanded to H heads."""
+    q = synth.gaussian(B, S, H, dqk, 128, seed)[0]
+    _, k, v = synth.gaussian(B, S, Hkv, dqk, 128, seed + 1)
+    gpu = []
+    for x in (q, k, v):
+        c, d = cfa.quantize_e4m3(torch.from_numpy(x).to(DEV))
+        gpu.append((c, float(d.item())))
+    torch.cuda.synchronize()
+    host = [oracle.quantize_e4m3(x) for x in (q, k, v)]
+    del q, k, v
+    for (gc, gd), (hc, hd) in zip(gpu, host):
+        assert gd == hd
+        assert np.array_equal(gc.view(torch.uint8).cpu().numpy(), hc)
+    (qg, dq), (kg, dk), (vg, dv) = gpu
+    c = 1.0 / math.sqrt(dqk)
+    out = torch.full((B, S, H, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((B, H, S), float("nan"), dtype=torch.float32, device=DEV)
+    cfa.attn_fwd_causal_fp8_ex(qg, kg, vg, dq, dk, dv, softmax_scale=c, p_mode=p_mode, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out.float()).any() and not torch.isnan(lse).any()
+    G = H // Hkv
+    qc = host[0][0]
+    kc, vc = (np.repeat(h[0], G, axis=2) for h in host[1:])
+    groups = sample_groups(B, H, S, n_groups, seed)
+    emu = oracle.emulate_fp8(qc, kc, vc, dq=dq, dk=dk, dv=dv, c=c, scheme=oracle.Fp8Scheme(exact_p=exact_p),
+                             groups=groups)
+    rows = oracle.group_rows(groups, 32)
+    ex, ex_lse = oracle.attn_exact(qc, kc, vc, dtype="fp8", c=c, dq=dq, dk=dk, dv=dv, rows=rows)
+    got, glse = gpu_rows(out, rows), lse_rows(lse, rows)
+    res = {"emu_maxabs": float(np.max(np.abs(got - emu["out"]))), "emu_rms": rms_rel(got, emu["out"]),
+           "fp64_rms": rms_rel(got, ex), "lse_emu": float(np.max(np.abs(glse - emu["lse"]))),
+           "lse_fp64": float(np.max(np.abs(glse - ex_lse)))}
+    print("RESULT", res, flush=True)
+    del out, lse, gpu
+    torch.cuda.empty_cache()
+    assert res["emu_maxabs"] <= TOL_EMU_MAXABS and res["emu_rms"] <= TOL_EMU_RMS, res
+    assert res["fp64_rms"] <= TOL_FP64_RMS_FP8, res
+    assert res["lse_emu"] <= LSE_EMU_NATS and res["lse_fp64"] <= LSE_FP64_NATS, res
+
+
+def test_fp8_gqa_b1_h32_hkv8_s32768():
+    _case("FP8 GQA B1 H32 Hkv8 S32768 d128 lean P (general entry point)")
+    _fp8_ex_full(1, 32, 8, 32768, 128, cfa.P_LEAN, False, 0, 12)
+
+
+def test_mla_lean_p_b1_h16_s32768():
+    _case("FP8 MLA B1 H16 S32768 192/128 lean P (general entry point)")
+    _fp8_ex_full(1, 16, 16, 32768, 192, cfa.P_LEAN, False, 0, 12)
+
+
+def test_bf16_mla_b1_h16_s32768():
+    _case("BF16 MLA B1 H16 S32768 192/128 (general entry point)")
+    B, H, S = 1, 16, 32768
+    q, k, v = synth.gaussian(B, S, H, 192, 128, 4)
+    gq, gk, gv = (cfa.round_bf16(torch.from_numpy(np.ascontiguousarray(x)).to(DEV)) for x in (q, k, v))
+    hq, hk, hv = (oracle.bf16_rne(x) for x in (q, k, v))
+    del q, k, v
+    c = 1 / math.sqrt(192)
+    out, lse = cfa.attn_fwd_causal_bf16_ex(gq, gk, gv, softmax_scale=c)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out.float()).any() and not torch.isnan(lse).any()
+    rows = oracle.group_rows(sample_groups(B, H, S, 12, 4), 32)
+    ex, ex_lse = oracle.attn_exact(hq, hk, hv, dtype="bf16", c=c, rows=rows)
+    got, glse = gpu_rows(out, rows), lse_rows(lse, rows)
+    res = {"fp64_rms": rms_rel(got, ex), "lse_fp64": float(np.max(np.abs(glse - ex_lse)))}
+    print("RESULT", res, flush=True)
+    assert res["fp64_rms"] <= TOL_FP64_RMS_BF16, res
+    assert res["lse_fp64"] <= 1e-3 + 1e-6 * np.max(np.abs(ex_lse)), res
