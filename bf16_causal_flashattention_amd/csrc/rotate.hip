@@ -295,7 +295,7 @@ __global__ void key_mean_final_kernel(const double* __restrict__ part, int S, in
 // keeps one head for all its items.
 int rot_grid(uint32_t n_items, uint32_t BH) {
   int64_t waves = 8192;
-  const int64_t per_head = 8192 / BH / 4 * 4;
+  const int64_t per_head = BH == 0 ? 0 : 8192 / BH / 4 * 4;
   if (per_head >= 4) waves = per_head * BH;
   if (waves > n_items) waves = ((int64_t)n_items + 3) / 4 * 4;
   if (waves < 4) waves = 4;

@@ -182,6 +182,9 @@ def test_rotation_prepass_validation():
     assert rq(None, None, FAKE, 1, 256, 1, 128, FAKE, FAKE, FAKE, None) == -1
     assert rq(FAKE, odd, FAKE, 1, 256, 1, 192, FAKE, FAKE, FAKE, None) == -3
     assert rq(FAKE, None, FAKE, 1 << 10, 1 << 12, 8, 128, FAKE, FAKE, FAKE, None) == -4
+    # empty tensors with no heads: nothing to rotate, and no host division by B*H
+    assert rq(None, None, FAKE, 0, 256, 0, 128, None, FAKE, FAKE, None) in (0, -6, -7)
+    assert rq(None, None, FAKE, 2, 256, 0, 192, None, FAKE, FAKE, None) in (0, -6, -7)
     rs = L.attn_rotate_quantize_e4m3_static
     for bad in (0.0, 3.0, -0.5, 2.0 ** 127, 2.0 ** -127, float("inf"), float("nan")):
         assert rs(FAKE, None, FAKE, 1, 256, 1, 128, bad, FAKE, None) == -5, bad

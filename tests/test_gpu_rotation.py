@@ -154,6 +154,10 @@ def test_rotate_quantize_degenerate():
     codes, ds = cfa.rotate_quantize_e4m3(torch.empty((1, 0, 2, D), dtype=torch.float32, device=DEV), sg)
     torch.cuda.synchronize()
     assert codes.numel() == 0 and float(ds.item()) == 1.0
+    _case("rotate_quantize no batch", D)
+    codes, ds = cfa.rotate_quantize_e4m3(torch.empty((0, 256, 2, D), dtype=torch.float32, device=DEV), sg)
+    torch.cuda.synchronize()
+    assert codes.numel() == 0 and float(ds.item()) == 1.0
     _case("rotate_quantize zeros", D)
     codes, ds = cfa.rotate_quantize_e4m3(torch.zeros((1, 64, 2, D), dtype=torch.float32, device=DEV), sg)
     torch.cuda.synchronize()
