@@ -119,10 +119,18 @@ def _outputs(q, v, out, lse):
     return out, lse
 
 
+def _same_device(*ts):
+    dev = ts[0].device
+    for t in ts:
+        if not t.is_cuda or t.device != dev:
+            raise ValueError("all tensors must be on the same GPU")
+
+
 def _meta(q, k, v, out, lse):
     for t in (q, k, v, out, lse):
         if t is not None and (not t.is_cuda or not t.is_contiguous()):
             raise ValueError("tensors must be contiguous and on the GPU")
+    _same_device(q, k, v, out, lse)
     if out.dtype != torch.bfloat16 or lse.dtype != torch.float32:
         raise TypeError("out must be bfloat16 and lse float32")
     B, S, H, dqk = q.shape
@@ -207,6 +215,7 @@ def _ex_meta(q, k, v, out, lse):
         raise TypeError("out must be bfloat16 and lse float32")
     if tuple(out.shape) != (B, S, H, dv) or tuple(lse.shape) != (B, H, S) or not lse.is_contiguous():
         raise ValueError("out / lse shapes disagree (lse must be a dense [B, H, S] tensor)")
+    _same_device(q, k, v, out, lse)
     st = [_strides(t) for t in (q, k, v, out)]
     return B, S, H, Hkv, dqk, dv, out, lse, st
 

@@ -250,3 +250,22 @@ def test_default_grid():
     assert cfa.default_grid(1, 32, 32768, 256) == 256
     assert cfa.default_grid(1, 1, 256, 256) == 1
     assert cfa.default_grid(1, 1, 300, 256) == -2
+
+
+def test_binding_rejects_host_tensors_before_any_call():
+    """The Python binding refuses tensors that are not on the GPU (here: all on the host),
+    so no host pointer ever reaches a kernel."""
+    import torch
+    q = torch.zeros((1, 256, 1, 128), dtype=torch.uint8)
+    with pytest.raises((ValueError, TypeError)):
+        cfa.attn_fwd_causal_fp8_ex(q, q, q, 1.0, 1.0, 1.0)
+    with pytest.raises((ValueError, TypeError)):
+        cfa.attn_fwd_causal_fp8(q, q, q, 1.0, 1.0, 1.0)
+    b = torch.zeros((1, 256, 1, 128), dtype=torch.bfloat16)
+    with pytest.raises((ValueError, TypeError)):
+        cfa.attn_fwd_causal_bf16_ex(b, b, b)
+    x = torch.zeros((1, 256, 1, 128), dtype=torch.float32)
+    for fn in (lambda: cfa.quantize_e4m3(x), lambda: cfa.round_bf16(x), lambda: cfa.key_mean(x),
+               lambda: cfa.quantize_e4m3_static(x, 1.0), lambda: cfa.rotate_quantize_e4m3(x, torch.ones(128))):
+        with pytest.raises((ValueError, TypeError)):
+            fn()
