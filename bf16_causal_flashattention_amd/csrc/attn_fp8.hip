@@ -57,9 +57,22 @@ constexpr float kLn2 = 0.69314718055994530942f;
 //   K slot: row 32*(key/32) + kinv(key%32) holds key `key` (kKCols data cells + 1 pad cell
 //           per row), so lane i of a wave reads row 32u + i, which holds key
 //           32u + key_perm_fp8(i).
-//   V slot: row r holds V[key0 + r][0..127] (8 data cells + 2 pad cells per row).  The PV
-//           operand V^T comes from ds_read_b64_tr_b8; the 160-byte row stride keeps those
-//           reads free of bank conflicts.
+//   V slot: 32 groups, each of four 128-byte rows (8 data cells each) and one pad cell, so
+//           row r starts at byte 128 r + 16 (r/4); then 32 spare cells (1088 cells, 17 DMA
+//           instructions of 64 cells).  Key 32a + 8b + c (c < 8) of the block lives in row
+//           32a + 8 (c%4) + c/4 + 2b.  The PV operand V^T comes from ds_read_b64_tr_b8: each
+//           instruction reads 8 consecutive keys, which this placement spreads over rows
+//           whose 16-byte cells fall in distinct bank groups (measured on gfx950: 192 bytes
+//           per clock and CU, against 178 for a uniform 160-byte row stride).
+// V slot placement: row of key k of the block, and its inverse
+__host__ __device__ constexpr int v_row_of_key(int k) {
+  return 32 * (k >> 5) + 8 * (k & 3) + ((k & 7) >> 2) + 2 * ((k >> 3) & 3);
+}
+__host__ __device__ constexpr int v_key_of_row(int r) {
+  return 32 * (r >> 5) + 8 * ((r & 7) >> 1) + ((r & 31) >> 3) + 4 * (r & 1);
+}
+__host__ __device__ constexpr int v_row_offset(int r) { return 128 * r + 16 * (r >> 2); }
+
 template <int DQK>
 struct Fp8Lds {
   static constexpr int kKCols = DQK / 16;
@@ -67,10 +80,13 @@ struct Fp8Lds {
   static constexpr int kKStride = 16 * kKSpr;
   static constexpr int kKCells = 128 * kKSpr;
   static constexpr int kKSlot = 16 * kKCells;
-  static constexpr int kVSpr = 10;
-  static constexpr int kVStride = 16 * kVSpr;
-  static constexpr int kVCells = 128 * kVSpr;
+  static constexpr int kVGroupCells = 33;  // 4 rows of 8 cells + 1 pad cell
+  static constexpr int kVCells = 1088;     // 32 groups + 32 spare cells (a whole last DMA instruction)
   static constexpr int kVSlot = 16 * kVCells;
+  // byte offsets of the transpose reads (see v_row_of_key): the 64 keys of scale block n start
+  // 8448 n bytes in; the four 8-key pieces of a lane half at keys +0, +8, +32, +40 lie 0, 256,
+  // 4224 and 4480 bytes from the first
+  static constexpr int kVHalf = 8448, kVPc8 = 256, kVPc32 = 4224, kVPc40 = 4480;
   static constexpr int kVBase = 2 * kKSlot;
   static constexpr int kBytes = 2 * kKSlot + 3 * kVSlot;
   static constexpr int kRounds = ((kKCells > kVCells ? kKCells : kVCells) + 255) / 256;  // DMA rounds, 256 threads
@@ -112,7 +128,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
   // (piece base) + s/2, bytes d0 + 8 (s%2) .. +7 with d0 = 32 dt + 16 ((lane/16) % 2); the
   // reading lane then holds d = 32 dt + lane%32 for 8 consecutive keys.  The four pieces of
   // a 64-key block n are keys 64n + 16 hh + {0, 8, 32, 40} + 0..7 (Sec. IV-A layout of P).
-  const int v_tr = L::kVBase + (16 * hh + ((lane & 15) >> 1)) * L::kVStride + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+  // source lane s of a 16-lane group reads key 16hh + s/2 (+ the piece and block offsets), in
+  // row v_row_of_key(16hh + s/2), bytes 16 ((lane/16) % 2) + 8 (s%2) of column group dt
+  const int v_tr = L::kVBase + v_row_offset(v_row_of_key(16 * hh + ((lane & 15) >> 1))) + 16 * ((lane >> 4) & 1) +
+                   8 * (lane & 1);
 
   // DMA assignments: the 256 threads of group 0 copy K blocks, those of group 1 V blocks.
   // Round p, thread st covers cell 256p + st of the slot; st_goff is its source offset
@@ -130,9 +149,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
     if (stage_k) {
       const int row = (cell / L::kKSpr) & 127, col = cell % L::kKSpr;
       st_goff[p] = ((row & ~31) | key_perm_fp8(row & 31)) * krs + 16 * (col < L::kKCols ? col : 0);
-    } else {
-      const int row = (cell / L::kVSpr) & 127, col = cell % L::kVSpr;
-      st_goff[p] = row * vrs + 16 * (col < 8 ? col : 0);
+    } else {  // pad and spare cells copy the block's first 16 bytes
+      const int g = cell / L::kVGroupCells, w = cell % L::kVGroupCells;
+      const bool data = g < 32 && w < 32;
+      st_goff[p] = data ? v_key_of_row(4 * g + w / 8) * vrs + 16 * (w % 8) : 0;
     }
   }
   const int st_lds = 16 * 64 * wq + (stage_k ? 0 : L::kVBase);
@@ -228,11 +248,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
         const uint8_t* sv = smem + (blk % 3) * L::kVSlot + v_tr;
         auto vread = [&](int t) {
           const int n = t / 4, dt = t % 4;
-          const uint8_t* p = sv + 64 * n * L::kVStride + 32 * dt;
+          const uint8_t* p = sv + L::kVHalf * n + 32 * dt;
           const v2i r0 = lds_tr8(p);
-          const v2i r1 = lds_tr8(p + 8 * L::kVStride);
-          const v2i r2 = lds_tr8(p + 32 * L::kVStride);
-          const v2i r3 = lds_tr8(p + 40 * L::kVStride);
+          const v2i r1 = lds_tr8(p + L::kVPc8);
+          const v2i r2 = lds_tr8(p + L::kVPc32);
+          const v2i r3 = lds_tr8(p + L::kVPc40);
           return (v8i){r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
         };
         v8i vop[2];
