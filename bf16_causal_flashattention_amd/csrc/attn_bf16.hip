@@ -92,6 +92,12 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// O staging for the epilogue: a 32-row area per wave with a 272-byte row pitch, so the
+// 16-byte pieces that 16 consecutive rows write at one column fall on distinct banks
+constexpr int kStgPitch = 272;
+constexpr int kStgWave = kWaveRows * kStgPitch;
+static_assert(kThreads / 64 * kStgWave <= Bf16Lds<128>::kLdsBytes, "O staging exceeds the LDS of the kernel");
+
 template <int DQK>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) {
   using L = Bf16Lds<DQK>;
@@ -339,9 +345,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
       }
       if (grp == 0) lds_barrier();
 
+      // epilogue: O through a per-wave LDS staging area, stored as whole 256-byte rows (the
+      // barrier at the end keeps the next tile's copies out until every wave has read its area)
       const float lt = sum_with_partner(l);
       const float inv = 1.0f / lt;
-      uint16_t* op = (uint16_t*)((uint8_t*)a.out + b * a.mo.sb + h * a.mo.sh + (int64_t)qrow * a.mo.ss);
+      uint8_t* stg = smem + wave * kStgWave;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -350,9 +358,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
           uint2 w;
           w.x = cvt_pk_bf16(oacc[dt][4 * g + 0] * inv, oacc[dt][4 * g + 1] * inv);
           w.y = cvt_pk_bf16(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
-          *(uint2*)(op + d0) = w;
+          *(uint2*)(stg + l32 * kStgPitch + 2 * d0) = w;
         }
+      {
+        uint8_t* orow = (uint8_t*)a.out + b * a.mo.sb + h * a.mo.sh + (int64_t)row0 * a.mo.ss;
+        const int sr = lane >> 4, sc = 16 * (lane & 15);
+#pragma unroll
+        for (int s4 = 0; s4 < kWaveRows / 4; ++s4) {
+          const int r = 4 * s4 + sr;
+          *(v4i*)(orow + (int64_t)r * a.mo.ss + sc) = *(const v4i*)(stg + r * kStgPitch + sc);
+        }
+      }
       if (a.lse != nullptr && hh == 0) a.lse[(int64_t)(b * H + h) * S + qrow] = kLn2 * (m + __log2f(lt));
+      lds_barrier();
     }
   }
 }

@@ -106,6 +106,12 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// O staging for the epilogue: a 32-row area per wave with a 272-byte row pitch, so the
+// 16-byte pieces that 16 consecutive rows write at one column fall on distinct banks
+constexpr int kStgPitch = 272;
+constexpr int kStgWave = kWaveRows * kStgPitch;
+static_assert(kThreads / 64 * kStgWave <= Fp8Lds<128>::kBytes, "O staging exceeds the LDS of the kernel");
+
 template <int DQK, bool EXACT_P, bool DEBUG>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
   using L = Fp8Lds<DQK>;
@@ -415,8 +421,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
       if (grp == 0) lds_barrier();
 
       // ---------------------------------------------------------------- epilogue
+      // O goes through LDS so that the stores are whole rows: each wave writes its 32 rows
+      // of bf16 O into a staging area of its own, then 16 lanes store each 256-byte row.
+      // Every operand read of the tile completed at the last barrier; the barrier after the
+      // stores keeps the next tile's copies out of LDS until every wave has read its area.
       const float inv = a.v_descale / l;
-      uint16_t* op = (uint16_t*)((uint8_t*)a.out + b * a.mo.sb + h * a.mo.sh + (int64_t)qrow * a.mo.ss);
+      uint8_t* stg = smem + wave * kStgWave;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -425,10 +435,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
           uint2 w;
           w.x = pack_bf16x2(oacc[dt][4 * g + 0] * inv, oacc[dt][4 * g + 1] * inv);
           w.y = pack_bf16x2(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
-          *(uint2*)(op + d0) = w;
+          *(uint2*)(stg + l32 * kStgPitch + 2 * d0) = w;
         }
+      {
+        uint8_t* orow = (uint8_t*)a.out + b * a.mo.sb + h * a.mo.sh + (int64_t)row0 * a.mo.ss;
+        const int sr = lane >> 4, sc = 16 * (lane & 15);
+#pragma unroll
+        for (int s4 = 0; s4 < kWaveRows / 4; ++s4) {
+          const int r = 4 * s4 + sr;
+          *(v4i*)(orow + (int64_t)r * a.mo.ss + sc) = *(const v4i*)(stg + r * kStgPitch + sc);
+        }
+      }
       if (a.lse != nullptr && hh == 0)
         a.lse[(int64_t)(b * H + h) * S + qrow] = kLn2 * (m + __log2f(l) - (float)kSigma);
+      lds_barrier();
     }
   }
 }
