@@ -26,6 +26,8 @@
 // K(i) (two K slots), group 1 copies V(i+2) into the slot of V(i-1) (three V slots); each
 // wave waits for its copies at the end of S_i.  Every target slot was last read in an
 // earlier phase and every copy completes at least one phase before its first read.
+// The epilogue stores O as whole rows through a per-wave LDS staging area, as in the FP8
+// kernel.
 //
 // fp32 arithmetic: t = s * cp with cp = fp32(c log2 e); p = exp2(fmaf(s, cp, -m));
 // l sums the fp32 p; P is p rounded to bf16; O = bf16(acc / l); LSE = ln 2 (m + log2 l).

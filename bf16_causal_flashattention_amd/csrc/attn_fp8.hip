@@ -28,6 +28,10 @@
 // the end of S_i.  Every target slot was last read in an earlier phase, every copy
 // completes at least one phase before its first read, and the softmax phase reads no
 // LDS, so nothing waits on a copy early.
+// Epilogue: after the tile's last barrier no wave reads K or V, so each wave writes its
+// 32 rows of bf16 O into a staging area of its own at the start of LDS and stores them
+// as whole 256-byte rows; a barrier keeps the next tile's copies out until every wave
+// has read its area.
 //
 // fp32 arithmetic (the order below is part of the contract with the test oracle):
 //   cp   = fp32(c * dq * dk * log2 e), scores s are fp32 MFMA sums
