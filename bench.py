@@ -56,17 +56,19 @@ def src_hash(path):
 
 
 class ClockSampler:
-    """Samples the shader clock with amd-smi while the timed window runs (best effort)."""
+    """Samples the shader clock (slowest XCD) and the socket power with amd-smi while the timed
+    window runs (best effort)."""
 
     def __init__(self):
         self.samples = []
+        self.power = []
         self._stop = threading.Event()
         self._t = None
 
     def _one(self):
         try:
-            r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"], capture_output=True, text=True,
-                               timeout=5)
+            r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "-p", "--json"], capture_output=True,
+                               text=True, timeout=5)
             data = json.loads(r.stdout)
             if isinstance(data, dict) and "gpu_data" in data:
                 data = data["gpu_data"]
@@ -83,6 +85,11 @@ class ClockSampler:
                         vals.append(float(cur))
             if vals:
                 self.samples.append(min(vals))
+            pw = data.get("power", {}).get("socket_power")
+            if isinstance(pw, dict):
+                pw = pw.get("value")
+            if pw not in (None, "N/A"):
+                self.power.append(float(pw))
         except Exception:
             pass
 
@@ -102,6 +109,9 @@ class ClockSampler:
 
     def median(self):
         return float(np.median(self.samples)) if self.samples else None
+
+    def median_power(self):
+        return float(np.median(self.power)) if self.power else None
 
 
 def time_launches(torch, fn, warmup, steps):
@@ -160,9 +170,12 @@ def sustained_window(torch, fn, F, chunk_s=0.5, window_s=3.0, max_warm_s=6.0):
         prev = cur
     with ClockSampler() as clk:
         ms, n = chunk(window_s)
-    return {"ms": round(ms, 4), "tflops": round(F / (ms * 1e-3) / 1e12, 2), "launches": n,
+    tflops = F / (ms * 1e-3) / 1e12
+    watts = clk.median_power()
+    return {"ms": round(ms, 4), "tflops": round(tflops, 2), "launches": n,
             "warm_in_s": round(time.time() - t0 - window_s, 2), "sclk_mhz_median_slowest_xcd": clk.median(),
-            "clock_samples": len(clk.samples)}
+            "clock_samples": len(clk.samples), "socket_power_w_median": watts,
+            "tflop_per_joule": round(tflops / watts, 3) if watts else None}
 
 
 def run_fp8(torch, cfa, kind, synth_fn, B, H, S, dqk, warmup, steps, seed=0, sustained=False):
