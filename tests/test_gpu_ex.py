@@ -47,6 +47,14 @@ def _out_like(B, S, H, layout):
     return _relayout(o, layout)
 
 
+def _assert_spare_heads_untouched(out, layout):
+    """With the padded layout, the kernel must not write the spare heads around the view."""
+    if layout == "padded":
+        base = out._base
+        assert base is not None and base.shape[2] == out.shape[2] + 2
+        assert not base[:, :, 0].view(torch.int16).any() and not base[:, :, -1].view(torch.int16).any()
+
+
 def _inputs(B, H, Hkv, S, dqk, seed):
     q = synth.gaussian(B, S, H, dqk, 128, seed)[0]
     _, k, v = synth.gaussian(B, S, Hkv, dqk, 128, seed + 1)
@@ -81,6 +89,7 @@ def test_fp8_ex(B, H, Hkv, S, dqk, p_mode, layout):
     cfa.attn_fwd_causal_fp8_ex(qL, kL, vL, dq, dk, dv, softmax_scale=c, p_mode=p_mode, out=out, lse=lse)
     torch.cuda.synchronize()
     assert not torch.isnan(out.float()).any() and not torch.isnan(lse).any()
+    _assert_spare_heads_untouched(out, layout)
 
     # bit-exact against the dense MHA path on expanded heads (same P mode)
     exact_p = (p_mode == cfa.P_EXACT) or (p_mode is None and dqk == 192)
@@ -158,6 +167,7 @@ def _bf16_ex_check(q, k, v, layout):
                                                    softmax_scale=c)
     torch.cuda.synchronize()
     assert not torch.isnan(out.float()).any() and not torch.isnan(lse).any()
+    _assert_spare_heads_untouched(out, layout)
     assert torch.equal(out.contiguous().view(torch.int16), ref_out.view(torch.int16))
     assert torch.equal(lse, ref_lse)
     if dqk == 128 and G == 1:
