@@ -400,7 +400,10 @@ def main():
     }
     if not args.only_headline:
         also = {}
-        wb, sb = max(3, args.warmup // 4), max(5, args.steps // 4)
+        # the paper's kernel-only burst protocol (Sec. V-B): 500 warm-up launches, then the
+        # mean of 100 (a short launch of S = 4K takes under 0.1 ms, so few launches would
+        # time a GPU still ramping its clock)
+        wb, sb = 500, 100
         r = run_bf16(torch, cfa, 1, 32, 32768, wb, sb, sustained=not args.no_sustained)
         also["bf16_B1_H32_S32768_d128"] = {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4),
                                            "pct_bf16_peak": round(100 * r["tflops"] / PEAK_TFLOPS["bf16"], 2),

@@ -84,6 +84,14 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// a barrier that leaves this wave's LDS reads in flight: for reads of data that no wave
+// overwrites before the reading wave's next barrier (the compiler waits for them at first use)
+__device__ __forceinline__ void barrier_reads_in_flight() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ v8bf as_bf(v4i x) { return __builtin_bit_cast(v8bf, x); }
 
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
@@ -342,8 +350,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
           probs();
         }
         if (i + 2 < nb) wait_dma();
-        if (live_n) preload(i + 1);  // V(i+1): its copy was waited for at least one phase ago
-        lds_barrier();
+        // V(i+1): its copy was waited for at least one phase ago, and its slot is next written
+        // in M_{i+2} (by V(i+4)), so the reads may complete after the barrier
+        if (live_n) preload(i + 1);
+        barrier_reads_in_flight();
       }
       if (grp == 0) lds_barrier();
 
