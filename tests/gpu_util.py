@@ -29,6 +29,14 @@ def rms_rel(a, b):
     return float(np.linalg.norm(a - b) / np.linalg.norm(b))
 
 
+def snr_db(got, ref):
+    """Signal-to-noise ratio of got against ref in dB: 10 log10(sum ref^2 / sum (got - ref)^2)."""
+    ref = np.asarray(ref, np.float64)
+    err = np.asarray(got, np.float64) - ref
+    e2 = float(np.sum(err * err))
+    return float("inf") if e2 == 0.0 else float(10 * np.log10(np.sum(ref * ref) / e2))
+
+
 def prep_fp8_gpu(q, k, v):
     """Quantise fp32 host arrays with the library's GPU quantiser."""
     outs = []

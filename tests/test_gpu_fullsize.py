@@ -15,7 +15,7 @@ import bf16_causal_flashattention_amd as cfa
 import oracle
 import synth
 from gpu_util import (DEV, LSE_EMU_NATS, LSE_FP64_NATS, TOL_EMU_MAXABS, TOL_EMU_RMS, TOL_FP64_RMS_BF16,
-                      TOL_FP64_RMS_FP8, gpu_rows, lse_rows, rms_rel, sample_groups)
+                      TOL_FP64_RMS_FP8, gpu_rows, lse_rows, rms_rel, sample_groups, snr_db)
 
 pytestmark = pytest.mark.gpu
 
@@ -52,7 +52,8 @@ def _fp8_full(gen, B, H, S, dqk, exact_p, seed, n_groups):
     ex, ex_lse = oracle.attn_exact(qc, kc, vc, dtype="fp8", c=c, dq=dq, dk=dk, dv=dv, rows=rows)
     got, glse = gpu_rows(out, rows), lse_rows(lse, rows)
     res = {"emu_maxabs": float(np.max(np.abs(got - emu["out"]))), "emu_rms": rms_rel(got, emu["out"]),
-           "fp64_rms": rms_rel(got, ex), "lse_emu": float(np.max(np.abs(glse - emu["lse"]))),
+           "fp64_rms": rms_rel(got, ex), "fp64_maxabs": float(np.max(np.abs(got - ex))),
+           "fp64_snr_db": snr_db(got, ex), "lse_emu": float(np.max(np.abs(glse - emu["lse"]))),
            "lse_fp64": float(np.max(np.abs(glse - ex_lse)))}
     print("RESULT", res, flush=True)
     del out, lse, gpu
@@ -102,7 +103,8 @@ def test_c3_bf16_b1_h32_sweep(S):
     rows = oracle.group_rows(sample_groups(B, H, S, 8, S), 32)
     ex, ex_lse = oracle.attn_exact(hq, hk, hv, dtype="bf16", c=1 / math.sqrt(128), rows=rows)
     got, glse = gpu_rows(out, rows), lse_rows(lse, rows)
-    res = {"fp64_rms": rms_rel(got, ex), "lse_fp64": float(np.max(np.abs(glse - ex_lse)))}
+    res = {"fp64_rms": rms_rel(got, ex), "fp64_maxabs": float(np.max(np.abs(got - ex))),
+           "fp64_snr_db": snr_db(got, ex), "lse_fp64": float(np.max(np.abs(glse - ex_lse)))}
     print("RESULT", res, flush=True)
     assert res["fp64_rms"] <= TOL_FP64_RMS_BF16 and res["lse_fp64"] <= 1e-3
     del out, lse, gq, gk, gv
@@ -141,7 +143,8 @@ def _fp8_ex_full(B, H, Hkv, S, dqk, p_mode, exact_p, seed, n_groups):
     ex, ex_lse = oracle.attn_exact(qc, kc, vc, dtype="fp8", c=c, dq=dq, dk=dk, dv=dv, rows=rows)
     got, glse = gpu_rows(out, rows), lse_rows(lse, rows)
     res = {"emu_maxabs": float(np.max(np.abs(got - emu["out"]))), "emu_rms": rms_rel(got, emu["out"]),
-           "fp64_rms": rms_rel(got, ex), "lse_emu": float(np.max(np.abs(glse - emu["lse"]))),
+           "fp64_rms": rms_rel(got, ex), "fp64_maxabs": float(np.max(np.abs(got - ex))),
+           "fp64_snr_db": snr_db(got, ex), "lse_emu": float(np.max(np.abs(glse - emu["lse"]))),
            "lse_fp64": float(np.max(np.abs(glse - ex_lse)))}
     print("RESULT", res, flush=True)
     del out, lse, gpu
@@ -175,7 +178,8 @@ def test_bf16_mla_b1_h16_s32768():
     rows = oracle.group_rows(sample_groups(B, H, S, 12, 4), 32)
     ex, ex_lse = oracle.attn_exact(hq, hk, hv, dtype="bf16", c=c, rows=rows)
     got, glse = gpu_rows(out, rows), lse_rows(lse, rows)
-    res = {"fp64_rms": rms_rel(got, ex), "lse_fp64": float(np.max(np.abs(glse - ex_lse)))}
+    res = {"fp64_rms": rms_rel(got, ex), "fp64_maxabs": float(np.max(np.abs(got - ex))),
+           "fp64_snr_db": snr_db(got, ex), "lse_fp64": float(np.max(np.abs(glse - ex_lse)))}
     print("RESULT", res, flush=True)
     assert res["fp64_rms"] <= TOL_FP64_RMS_BF16, res
     assert res["lse_fp64"] <= 1e-3 + 1e-6 * np.max(np.abs(ex_lse)), res
