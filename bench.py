@@ -11,7 +11,8 @@ the BF16 kernel at the same shape, the MLA-shaped FP8 kernel (B=1, H=16, S=32768
 host cores over a bounded sample of the headline workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only-headline] [--no-cpu-baseline]
-Prints one JSON line.
+       python bench.py --line {act,bf16,bf16_mla,fp8_4k,gqa,mla,mla_lean} [--steps K] [--warmup W]
+Prints one JSON line (with --line: that configuration's time alone, for profiler runs).
 """
 from __future__ import annotations
 
@@ -337,6 +338,18 @@ def traffic_entry():
         return None
 
 
+# single configurations for --line: (torch, cfa, synth, warmup, steps) -> result of the run_* helper
+LINES = {
+    "bf16": lambda t, c, sy, w, n: run_bf16(t, c, 1, 32, 32768, w, n),
+    "mla": lambda t, c, sy, w, n: run_fp8(t, c, "mla", sy.gaussian, 1, 16, 32768, 192, w, n),
+    "mla_lean": lambda t, c, sy, w, n: run_fp8_ex(t, c, 1, 16, 16, 32768, 192, c.P_LEAN, w, n),
+    "bf16_mla": lambda t, c, sy, w, n: run_bf16(t, c, 1, 16, 32768, w, n, dqk=192),
+    "gqa": lambda t, c, sy, w, n: run_fp8_ex(t, c, 1, 32, 8, 32768, 128, c.P_LEAN, w, n),
+    "act": lambda t, c, sy, w, n: run_fp8(t, c, "fp8", sy.activation_like, 1, 32, 16384, 128, w, n),
+    "fp8_4k": lambda t, c, sy, w, n: run_fp8(t, c, "fp8", sy.gaussian, 1, 32, 4096, 128, w, n),
+}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -346,6 +359,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sustained", action="store_true", help="skip the sustained-clock window")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--line", choices=sorted(LINES),
+                    help="time one other configuration alone with --warmup/--steps and print its result "
+                         "(for profiler and counter runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -369,6 +385,11 @@ def main():
         torch.cuda.synchronize()
         log("copy calibration: 3 copies of 2^30 bytes")
         del x, y
+    if args.line:
+        r = LINES[args.line](torch, cfa, synth, args.warmup, args.steps)
+        print(json.dumps({"line": args.line, "ms": round(r["ms"], 4), "tflops": round(r["tflops"], 2),
+                          "warmup": args.warmup, "steps": args.steps}), flush=True)
+        return
     B, H, S, D = 1, 32, 32768, 128
     head = run_fp8(torch, cfa, "fp8", synth.gaussian, B, H, S, D, args.warmup, args.steps,
                    sustained=not args.no_sustained)

@@ -51,8 +51,12 @@ constexpr float kLn2 = 0.69314718055994530942f;
 //           involution), d_qk/8 + 1 cells per row (272 bytes at d_qk = 128, 400 at 192;
 //           both keep each 16-lane group of a 16-byte read on distinct banks), so lane i
 //           reads row 32u + i, which holds key 32u + key_perm_bf16(i).
-//   V slot: row r holds V[key0 + r][0..127], 18 cells (288 bytes) per row; the PV operand
-//           (V^T) comes from LDS transpose reads.
+//   V slot: row r holds V[key0 + r][0..127], 20 cells (320 bytes) per row; the PV operand
+//           (V^T) comes from LDS transpose reads.  A transpose read takes 8 bytes per lane
+//           from 4 consecutive rows per 16-lane group, and the two 16-lane groups of a lane
+//           half read neighbouring 32-byte pieces of the same rows; with a 320-byte stride the
+//           8 pieces of 32 lanes fall on distinct banks (a 288-byte stride made them collide,
+//           measured as 5.4e8 bank-conflict cycles per call at B1 H32 S32768, now 3e6).
 constexpr int kBlk = 64;  // keys per block (max update, ping-pong phase and LDS slot)
 template <int DQK>
 struct Bf16Lds {
@@ -61,7 +65,7 @@ struct Bf16Lds {
   static constexpr int kKStride = 16 * kKSpr;
   static constexpr int kKCells = kBlk * kKSpr;
   static constexpr int kKSlot = 16 * kKCells;
-  static constexpr int kVSpr = 18;
+  static constexpr int kVSpr = 20;
   static constexpr int kVStride = 16 * kVSpr;
   static constexpr int kVCells = kBlk * kVSpr;
   static constexpr int kVSlot = 16 * kVCells;
