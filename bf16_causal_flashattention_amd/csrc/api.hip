@@ -353,13 +353,13 @@ int64_t attn_schedule(int B, int H, int S, int grid, int32_t* records, int64_t c
   if (!records || cap < need) return ATTN_ERR_ARG;
   int64_t n = 0;
   for (int bid = 0; bid < grid; ++bid) {
-    const int logical = cfa::xcd_logical(bid, grid);
-    for (int64_t item = logical; item < s.items; item += grid) {
+    const cfa::ItemRange work = cfa::xcd_items(bid, grid, s.items);
+    for (int64_t item = work.first; item < work.end; item += work.step) {
       int b, h, j;
       cfa::decode_item(item, H, s.P, b, h, j);
       for (int pass = 0; pass < 2; ++pass) {
-        const int tile = pass == 0 ? j : s.T - 1 - j;
-        if (pass == 1 && tile == j) break;
+        const int tile = pass == 0 ? s.T - 1 - j : j;
+        if (pass == 1 && tile == s.T - 1 - j) break;
         if (n >= need) return ATTN_ERR_ARG;  // would mean a tile is visited twice
         records[4 * n + 0] = bid;
         records[4 * n + 1] = b;

@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
   const int grp = wave >> 2;
   const int S = a.S, H = a.H;
   const Schedule sch = make_schedule(a.B, H, S);
-  const int logical = xcd_logical(blockIdx.x, gridDim.x);
+  const ItemRange work = xcd_items(blockIdx.x, gridDim.x, sch.items);
   const int krs = a.mk.ss, vrs = a.mv.ss;  // key / value row strides in bytes
 
   const int k_rd = l32 * kKStride + 16 * hh;
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
   const v16f zero16 = {};
   const float cp = a.cp;
 
-  for (int64_t item = logical; item < sch.items; item += gridDim.x) {
+  for (int64_t item = work.first; item < work.end; item += work.step) {
     int b, h, j;
     decode_item(item, H, sch.P, b, h, j);
     const int hk = h / a.G;  // key/value head of query head h
@@ -170,8 +170,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
     const int st_rs = stage_k ? krs : vrs;
 
     for (int pass = 0; pass < 2; ++pass) {
-      const int tile = pass == 0 ? j : sch.T - 1 - j;
-      if (pass == 1 && tile == j) break;
+      // the long tile of the pair first: the workgroups of one XCD then start on key block 0
+      // together and read the same K/V blocks from its L2 for most of that tile
+      const int tile = pass == 0 ? sch.T - 1 - j : j;
+      if (pass == 1 && tile == sch.T - 1 - j) break;
       const int row0 = tile * kTileRows + wave * kWaveRows;
       const int qrow = row0 + l32;
       const int nb = 4 * tile + 4;  // 64-key blocks

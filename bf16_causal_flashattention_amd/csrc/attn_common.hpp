@@ -30,12 +30,18 @@ constexpr int kXcds = 8;
 // ---------------------------------------------------------------------------
 // Work decomposition (Sec. IV-A, "Causal pairing" and "Chiplet placement").
 // Per (b, h) there are T = S / 256 query tiles.  Work item j of a head runs tile
-// j and then tile T-1-j, so every item covers T+1 key steps of 256; when T is odd
-// the middle tile runs alone.  Items are numbered head-major, pairs contiguous:
+// T-1-j and then tile j, so every item covers T+1 key steps of 256; when T is odd
+// the middle tile runs alone.  The long tile comes first, so that the workgroups of an
+// XCD, which start together on neighbouring items of one head, read the same K/V blocks
+// at about the same time for most of it.  Items are numbered head-major, pairs contiguous:
 //   item = (b * H + h) * P + j,  P = ceil(T / 2).
-// A persistent grid of G workgroups walks the items with stride G.  The hardware
-// dispatches workgroup i to XCD i mod 8; the remap below gives each XCD a run of
-// consecutive logical ids, so consecutive pairs of one head share an L2.
+// A persistent grid of G workgroups covers the N items.  The hardware dispatches
+// workgroup i to XCD i mod 8; XCD x, with n_x = G/8 + (x < G%8) workgroups, owns the
+// contiguous item range [N p_x / G, N (p_x + n_x) / G), where p_x counts the workgroups
+// of the XCDs below x, and its w-th workgroup takes items first + w, first + w + n_x, ...
+// So the workgroups of one XCD always work on neighbouring items, the tile pairs of one
+// or two heads, whose K and V blocks then stream through that XCD's L2 once.  The ranges
+// follow the workgroup counts, so no workgroup gets more than ceil(N / G) items.
 struct Schedule {
   int T;          // tiles per head
   int P;          // items per head
@@ -50,13 +56,29 @@ __host__ __device__ inline Schedule make_schedule(int B, int H, int S) {
   return s;
 }
 
-// Bijection from the dispatch index to a logical index, for any grid size G:
-// XCD x holds n_x = G/8 + (x < G%8) workgroups and takes logical ids
-// [x*(G/8) + min(x, G%8), ... + n_x).
-__host__ __device__ inline int xcd_logical(int bid, int grid) {
+// the items of workgroup bid of a grid of G: first, first + step, ... below end
+struct ItemRange {
+  int64_t first, end;
+  int step;
+};
+
+__host__ __device__ inline ItemRange xcd_items(int bid, int grid, int64_t items) {
   const int per = grid / kXcds, rem = grid % kXcds;
-  const int x = bid % kXcds, idx = bid / kXcds;
-  return x * per + (x < rem ? x : rem) + idx;
+  const int x = bid % kXcds, w = bid / kXcds;
+  const int n = per + (x < rem ? 1 : 0);
+  const int64_t p0 = (int64_t)x * per + (x < rem ? x : rem);
+  ItemRange r;
+  const uint64_t a = (uint64_t)items * (uint64_t)p0, b = (uint64_t)items * (uint64_t)(p0 + n);
+  if (b < (UINT64_C(1) << 32)) {  // the usual case: 32-bit divisions (a 64-bit one is slow on the GPU)
+    r.first = (uint32_t)a / (uint32_t)grid;
+    r.end = (uint32_t)b / (uint32_t)grid;
+  } else {
+    r.first = (int64_t)(a / (uint64_t)grid);
+    r.end = (int64_t)(b / (uint64_t)grid);
+  }
+  r.first += w;
+  r.step = n;
+  return r;
 }
 
 __host__ __device__ inline void decode_item(int64_t item, int H, int P, int& b, int& h, int& j) {

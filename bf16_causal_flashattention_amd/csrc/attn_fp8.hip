@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
   const int grp = wave >> 2;  // 0: waves 0-3, 1: waves 4-7 (one of each per SIMD)
   const int S = a.S, H = a.H;
   const Schedule sch = make_schedule(a.B, H, S);
-  const int logical = xcd_logical(blockIdx.x, gridDim.x);
+  const ItemRange work = xcd_items(blockIdx.x, gridDim.x, sch.items);
 
   const int krs = a.mk.ss, vrs = a.mv.ss;  // key / value row strides in bytes
 
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
   const float cp = a.cp;
   const float cp8 = 8.0f * cp;
 
-  for (int64_t item = logical; item < sch.items; item += gridDim.x) {
+  for (int64_t item = work.first; item < work.end; item += work.step) {
     int b, h, j;
     decode_item(item, H, sch.P, b, h, j);
     const int hk = h / a.G;  // key/value head of query head h
@@ -186,8 +186,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
     const int st_rs = stage_k ? krs : vrs;
 
     for (int pass = 0; pass < 2; ++pass) {
-      const int tile = pass == 0 ? j : sch.T - 1 - j;
-      if (pass == 1 && tile == j) break;
+      // the long tile of the pair first: the workgroups of one XCD then start on key block 0
+      // together and read the same K/V blocks from its L2 for most of that tile
+      const int tile = pass == 0 ? sch.T - 1 - j : j;
+      if (pass == 1 && tile == sch.T - 1 - j) break;
       const int row0 = tile * kTileRows + wave * kWaveRows;  // first query row of this wave
       const int qrow = row0 + l32;
       const int nb = 2 * tile + 2;                             // 128-key blocks
