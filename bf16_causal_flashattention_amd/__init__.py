@@ -92,7 +92,12 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream():
+def _stream(t):
+    """The current HIP stream of the current device, which must be the device of tensor t
+    (the library launches on the current device)."""
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"tensors are on {t.device} but the current device is cuda:{torch.cuda.current_device()}; "
+                         f"call under torch.cuda.device({t.device.index})")
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
@@ -152,7 +157,7 @@ def _fp8_call(fn_name, q, k, v, q_descale, k_descale, v_descale, softmax_scale, 
             float(v_descale), float(softmax_scale), B, H, S, dqk, dv]
     if debug is not None:
         args += [_ptr(debug[0]), _ptr(debug[1])]
-    _check(fn_name, getattr(lib(), fn_name)(*args, _stream()))
+    _check(fn_name, getattr(lib(), fn_name)(*args, _stream(q)))
     return out, lse
 
 
@@ -187,7 +192,7 @@ def attn_fwd_causal_bf16(q, k, v, softmax_scale=None, out=None, lse=None):
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(dqk)
     rc = lib().attn_fwd_causal_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), float(softmax_scale),
-                                    B, H, S, dqk, dv, _stream())
+                                    B, H, S, dqk, dv, _stream(q))
     _check("attn_fwd_causal_bf16", rc)
     return out, lse
 
@@ -231,7 +236,7 @@ def attn_fwd_causal_fp8_ex(q, k, v, q_descale, k_descale, v_descale, softmax_sca
     pm = P_DEFAULT if p_mode is None else int(p_mode)
     rc = lib().attn_fwd_causal_fp8_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), float(q_descale),
                                       float(k_descale), float(v_descale), float(softmax_scale), B, H, Hkv, S, dqk,
-                                      dv, *[ctypes.byref(x) for x in st], pm, _stream())
+                                      dv, *[ctypes.byref(x) for x in st], pm, _stream(q))
     _check("attn_fwd_causal_fp8_ex", rc)
     return out, lse
 
@@ -245,7 +250,7 @@ def attn_fwd_causal_bf16_ex(q, k, v, softmax_scale=None, out=None, lse=None):
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(dqk)
     rc = lib().attn_fwd_causal_bf16_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), float(softmax_scale),
-                                       B, H, Hkv, S, dqk, dv, *[ctypes.byref(x) for x in st], _stream())
+                                       B, H, Hkv, S, dqk, dv, *[ctypes.byref(x) for x in st], _stream(q))
     _check("attn_fwd_causal_bf16_ex", rc)
     return out, lse
 
@@ -260,7 +265,7 @@ def quantize_e4m3(x, workspace=None):
     descale = torch.empty(1, dtype=torch.float32, device=x.device)
     if workspace is None:
         workspace = torch.empty(1, dtype=torch.int32, device=x.device)
-    rc = lib().attn_quantize_e4m3(_ptr(x), x.numel(), _ptr(codes), _ptr(descale), _ptr(workspace), _stream())
+    rc = lib().attn_quantize_e4m3(_ptr(x), x.numel(), _ptr(codes), _ptr(descale), _ptr(workspace), _stream(x))
     _check("attn_quantize_e4m3", rc)
     return codes.view(torch.float8_e4m3fn), descale
 
@@ -280,7 +285,7 @@ def key_mean(k):
         raise AttnError("attn_key_mean_workspace", int(n_ws))
     mean = torch.empty((B, H, D), dtype=torch.float32, device=k.device)
     ws = torch.empty(max((int(n_ws) + 7) // 8, 1), dtype=torch.float64, device=k.device)
-    _check("attn_key_mean", L.attn_key_mean(_ptr(k), B, S, H, D, _ptr(mean), _ptr(ws), _stream()))
+    _check("attn_key_mean", L.attn_key_mean(_ptr(k), B, S, H, D, _ptr(mean), _ptr(ws), _stream(k)))
     return mean
 
 
@@ -300,7 +305,7 @@ def quantize_e4m3_static(x, descale):
     if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
         raise TypeError("x must be a contiguous float32 GPU tensor")
     codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
-    rc = lib().attn_quantize_e4m3_static(_ptr(x), x.numel(), float(descale), _ptr(codes), _stream())
+    rc = lib().attn_quantize_e4m3_static(_ptr(x), x.numel(), float(descale), _ptr(codes), _stream(x))
     _check("attn_quantize_e4m3_static", rc)
     return codes.view(torch.float8_e4m3fn)
 
@@ -311,7 +316,7 @@ def rotate_quantize_e4m3_static(x, signs, descale, mean=None):
     B, S, H, D = _rot_checks(x, signs, mean)
     codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     rc = lib().attn_rotate_quantize_e4m3_static(_ptr(x), _ptr(mean), _ptr(signs), B, S, H, D, float(descale),
-                                                _ptr(codes), _stream())
+                                                _ptr(codes), _stream(x))
     _check("attn_rotate_quantize_e4m3_static", rc)
     return codes.view(torch.float8_e4m3fn)
 
@@ -327,7 +332,7 @@ def rotate_quantize_e4m3(x, signs, mean=None, workspace=None):
     if workspace is None:
         workspace = torch.empty(1, dtype=torch.int32, device=x.device)
     rc = lib().attn_rotate_quantize_e4m3(_ptr(x), _ptr(mean), _ptr(signs), B, S, H, D, _ptr(codes), _ptr(descale),
-                                         _ptr(workspace), _stream())
+                                         _ptr(workspace), _stream(x))
     _check("attn_rotate_quantize_e4m3", rc)
     return codes.view(torch.float8_e4m3fn), descale
 
@@ -337,7 +342,7 @@ def round_bf16(x):
     if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
         raise TypeError("x must be a contiguous float32 GPU tensor")
     out = torch.empty(x.shape, dtype=torch.int16, device=x.device)
-    _check("attn_round_bf16", lib().attn_round_bf16(_ptr(x), x.numel(), _ptr(out), _stream()))
+    _check("attn_round_bf16", lib().attn_round_bf16(_ptr(x), x.numel(), _ptr(out), _stream(x)))
     return out.view(torch.bfloat16)
 
 

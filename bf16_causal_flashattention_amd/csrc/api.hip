@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "attn_common.hpp"
 #include "attn_fwd_causal.h"
 #include "attn_launch.hpp"
@@ -12,7 +14,9 @@ namespace {
 
 constexpr double kLog2e = 1.4426950408889634074;
 constexpr int kMaxDevices = 64;
-int g_num_cu[kMaxDevices];  // cached compute-unit count per device (0 = unknown)
+// cached compute-unit count per device (0 = unknown); atomic because the entry points may be
+// called from several host threads at once
+std::atomic<int> g_num_cu[kMaxDevices];
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 bool good_scale(float s) { return isfinite(s) && s > 0.0f; }
@@ -100,14 +104,14 @@ Problem make_problem(const void* q, const void* k, const void* v, void* out, flo
 int device_cu_count(int* n) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return ATTN_ERR_DEVICE;
-  if (dev < kMaxDevices && g_num_cu[dev] > 0) {
-    *n = g_num_cu[dev];
+  if (dev < kMaxDevices && g_num_cu[dev].load(std::memory_order_relaxed) > 0) {
+    *n = g_num_cu[dev].load(std::memory_order_relaxed);
     return ATTN_OK;
   }
   int cu = 0;
   if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0)
     return ATTN_ERR_DEVICE;
-  if (dev < kMaxDevices) g_num_cu[dev] = cu;
+  if (dev < kMaxDevices) g_num_cu[dev].store(cu, std::memory_order_relaxed);
   *n = cu;
   return ATTN_OK;
 }
