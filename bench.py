@@ -143,10 +143,27 @@ def prep_fp8(torch, cfa, synth_fn, B, S, H, dqk, dv, seed):
     return tens, [o[0] for o in out], [float(o[1].item()) for o in out], prep
 
 
-def sustained_window(torch, fn, F, chunk_s=0.5, window_s=3.0, max_warm_s=6.0):
-    """Sustained-clock timing (paper Sec. V-C): back-to-back launches in 0.5 s chunks until
-    two consecutive chunks agree within 0.3% (at least 1 s), then a timed window of about
-    window_s seconds while amd-smi samples the shader clock (slowest XCD per sample)."""
+def sustained(torch, fn, F, reps=1):
+    """Sustained-clock timing as in the paper (Sec. V-B): `reps` runs, each after 2 s of idle,
+    of sustained_window; reports the median run (by time) with the range over the runs."""
+    runs = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        time.sleep(2.0)
+        runs.append(sustained_window(torch, fn, F))
+    runs.sort(key=lambda r: r["ms"])
+    med = dict(runs[len(runs) // 2])
+    med["repetitions"] = len(runs)
+    med["tflops_range"] = [runs[-1]["tflops"], runs[0]["tflops"]]
+    med["sclk_mhz_range"] = [min((r["sclk_mhz_median_slowest_xcd"] or 0) for r in runs),
+                             max((r["sclk_mhz_median_slowest_xcd"] or 0) for r in runs)]
+    return med
+
+
+def sustained_window(torch, fn, F, chunk_s=0.5, window_s=4.0, max_warm_s=6.0):
+    """One sustained-clock run: back-to-back launches in 0.5 s chunks until two consecutive
+    chunks agree within 0.3% (at least 1 s), then a timed window of about window_s seconds
+    while amd-smi samples the shader clock (slowest XCD per sample) and the socket power."""
     def chunk(seconds):
         # launches per chunk from a short probe
         stream = torch.cuda.current_stream()
@@ -179,7 +196,7 @@ def sustained_window(torch, fn, F, chunk_s=0.5, window_s=3.0, max_warm_s=6.0):
             "tflop_per_joule": round(tflops / watts, 3) if watts else None}
 
 
-def run_fp8(torch, cfa, kind, synth_fn, B, H, S, dqk, warmup, steps, seed=0, sustained=False):
+def run_fp8(torch, cfa, kind, synth_fn, B, H, S, dqk, warmup, steps, seed=0, sustained_reps=0):
     log(f"{kind} B={B} H={H} S={S} d_qk={dqk}: generating inputs")
     tens, codes, ds, prep = prep_fp8(torch, cfa, synth_fn, B, S, H, dqk, 128, seed)
     qg, kg, vg = codes
@@ -193,8 +210,8 @@ def run_fp8(torch, cfa, kind, synth_fn, B, H, S, dqk, warmup, steps, seed=0, sus
     F = flops(B, H, S, dqk, 128)
     res = {"ms": ms, "tflops": F / (ms * 1e-3) / 1e12, "prep_ms": prep_ms,
            "bytes": fp8_hbm_bytes(B, H, S, dqk, 128, 1)}
-    if sustained:
-        res["sustained"] = sustained_window(torch, fn, F)
+    if sustained_reps:
+        res["sustained"] = sustained(torch, fn, F, sustained_reps)
     del tens
     return res
 
@@ -222,7 +239,7 @@ def run_fp8_ex(torch, cfa, B, H, Hkv, S, dqk, p_mode, warmup, steps, seed=0):
     return {"ms": ms, "tflops": F / (ms * 1e-3) / 1e12}
 
 
-def run_bf16(torch, cfa, B, H, S, warmup, steps, seed=0, sustained=False, dqk=128):
+def run_bf16(torch, cfa, B, H, S, warmup, steps, seed=0, sustained_reps=0, dqk=128):
     import synth
     log(f"bf16 B={B} H={H} S={S} d_qk={dqk}: generating inputs")
     q, k, v = synth.gaussian(B, S, H, dqk, 128, seed)
@@ -240,8 +257,8 @@ def run_bf16(torch, cfa, B, H, S, warmup, steps, seed=0, sustained=False, dqk=12
     F = flops(B, H, S, dqk, 128)
     log(f"bf16 B={B} H={H} S={S} d_qk={dqk}: {ms:.4f} ms/launch")
     res = {"ms": ms, "tflops": F / (ms * 1e-3) / 1e12}
-    if sustained:
-        res["sustained"] = sustained_window(torch, fn, F)
+    if sustained_reps:
+        res["sustained"] = sustained(torch, fn, F, sustained_reps)
     return res
 
 
@@ -392,7 +409,7 @@ def main():
         return
     B, H, S, D = 1, 32, 32768, 128
     head = run_fp8(torch, cfa, "fp8", synth.gaussian, B, H, S, D, args.warmup, args.steps,
-                   sustained=not args.no_sustained)
+                   sustained_reps=0 if args.no_sustained else 3)
     F = flops(B, H, S, D, D)
     achieved = F / (head["ms"] * 1e-3) / 1e12
     result = {
@@ -425,7 +442,7 @@ def main():
         # mean of 100 (a short launch of S = 4K takes under 0.1 ms, so few launches would
         # time a GPU still ramping its clock)
         wb, sb = 500, 100
-        r = run_bf16(torch, cfa, 1, 32, 32768, wb, sb, sustained=not args.no_sustained)
+        r = run_bf16(torch, cfa, 1, 32, 32768, wb, sb, sustained_reps=0 if args.no_sustained else 1)
         also["bf16_B1_H32_S32768_d128"] = {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4),
                                            "pct_bf16_peak": round(100 * r["tflops"] / PEAK_TFLOPS["bf16"], 2),
                                            "sustained": r.get("sustained")}
@@ -434,7 +451,8 @@ def main():
             also[f"bf16_B1_H32_S{s}_d128"] = {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4)}
             r = run_fp8(torch, cfa, "fp8", synth.gaussian, 1, 32, s, 128, wb, sb)
             also[f"fp8_B1_H32_S{s}_d128"] = {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4)}
-        r = run_fp8(torch, cfa, "mla", synth.gaussian, 1, 16, 32768, 192, wb, sb, sustained=not args.no_sustained)
+        r = run_fp8(torch, cfa, "mla", synth.gaussian, 1, 16, 32768, 192, wb, sb,
+                    sustained_reps=0 if args.no_sustained else 1)
         also["mla_fp8_B1_H16_S32768_192_128"] = {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4),
                                                   "pct_fp8_peak": round(100 * r["tflops"] / PEAK_TFLOPS["fp8"], 2),
                                                   "sustained": r.get("sustained")}
