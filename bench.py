@@ -239,10 +239,10 @@ def run_fp8_ex(torch, cfa, B, H, Hkv, S, dqk, p_mode, warmup, steps, seed=0):
     return {"ms": ms, "tflops": F / (ms * 1e-3) / 1e12}
 
 
-def run_bf16(torch, cfa, B, H, S, warmup, steps, seed=0, sustained_reps=0, dqk=128):
+def run_bf16(torch, cfa, B, H, S, warmup, steps, seed=0, sustained_reps=0, dqk=128, std=1.0):
     import synth
-    log(f"bf16 B={B} H={H} S={S} d_qk={dqk}: generating inputs")
-    q, k, v = synth.gaussian(B, S, H, dqk, 128, seed)
+    log(f"bf16 B={B} H={H} S={S} d_qk={dqk} std={std}: generating inputs")
+    q, k, v = synth.gaussian(B, S, H, dqk, 128, seed, std=std)
     dev = torch.device("cuda:0")
     tens = [torch.from_numpy(x).to(dev) for x in (q, k, v)]
     del q, k, v
@@ -467,6 +467,15 @@ def main():
                                                     "pct_fp8_peak": round(100 * r["tflops"] / PEAK_TFLOPS["fp8"], 2)}
         r = run_fp8(torch, cfa, "fp8", synth.activation_like, 1, 32, 16384, 128, wb, sb)
         also["fp8_activation_like_B1_H32_S16384_d128"] = {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4)}
+        # the paper's own timing inputs, N(0, 0.1^2): nearly uniform probabilities, so other
+        # operand bits switch and the clock differs (Sec. III-C)
+        gauss01 = lambda B_, S_, H_, dqk_, dv_, seed_: synth.gaussian(B_, S_, H_, dqk_, dv_, seed_, std=0.1)
+        r = run_fp8(torch, cfa, "fp8", gauss01, 1, 32, 32768, 128, wb, sb)
+        also["fp8_B1_H32_S32768_d128_gaussian_sd0.1"] = {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4),
+                                                         "pct_fp8_peak": round(100 * r["tflops"] / PEAK_TFLOPS["fp8"], 2)}
+        r = run_bf16(torch, cfa, 1, 32, 32768, wb, sb, std=0.1)
+        also["bf16_B1_H32_S32768_d128_gaussian_sd0.1"] = {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4),
+                                                          "pct_bf16_peak": round(100 * r["tflops"] / PEAK_TFLOPS["bf16"], 2)}
         also["prepass_rotate_smooth_B1_H32_S32768_d128"] = run_rotate_prepass(torch, cfa, 1, 32, 32768, 128, wb, sb)
         also["prepass_rotate_smooth_B1_H16_S32768_d192"] = run_rotate_prepass(torch, cfa, 1, 16, 32768, 192, wb, sb)
         result["also"] = also
