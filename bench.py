@@ -196,7 +196,10 @@ def sustained_window(torch, fn, F, chunk_s=0.5, window_s=4.0, max_warm_s=6.0):
             "tflop_per_joule": round(tflops / watts, 3) if watts else None}
 
 
-def run_fp8(torch, cfa, kind, synth_fn, B, H, S, dqk, warmup, steps, seed=0, sustained_reps=0):
+def run_fp8(torch, cfa, kind, synth_fn, B, H, S, dqk, warmup, steps, seed=0, sustained_reps=0,
+            v_channel_major=False):
+    """FP8 attention through the basic entry point, or with v_channel_major through the entry
+    point that takes V as [B, H, 128, S] (the transposed copy is made before the timing)."""
     log(f"{kind} B={B} H={H} S={S} d_qk={dqk}: generating inputs")
     tens, codes, ds, prep = prep_fp8(torch, cfa, synth_fn, B, S, H, dqk, 128, seed)
     qg, kg, vg = codes
@@ -204,6 +207,9 @@ def run_fp8(torch, cfa, kind, synth_fn, B, H, S, dqk, warmup, steps, seed=0, sus
     lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda:0")
     entry = cfa.attn_fwd_causal_fp8 if dqk == 128 else cfa.attn_fwd_causal_mla
     fn = lambda: entry(qg, kg, vg, ds[0], ds[1], ds[2], out=out, lse=lse)
+    if v_channel_major:
+        vt = vg.view(torch.uint8).permute(0, 2, 3, 1).contiguous()
+        fn = lambda: cfa.attn_fwd_causal_fp8_vt(qg, kg, vt, ds[0], ds[1], ds[2], out=out, lse=lse)
     ms = time_launches(torch, fn, warmup, steps)
     prep_ms = time_launches(torch, prep, 2, 5)
     log(f"{kind} B={B} H={H} S={S} d_qk={dqk}: {ms:.4f} ms/launch")
@@ -363,6 +369,7 @@ LINES = {
     "bf16_mla": lambda t, c, sy, w, n: run_bf16(t, c, 1, 16, 32768, w, n, dqk=192),
     "gqa": lambda t, c, sy, w, n: run_fp8_ex(t, c, 1, 32, 8, 32768, 128, c.P_LEAN, w, n),
     "act": lambda t, c, sy, w, n: run_fp8(t, c, "fp8", sy.activation_like, 1, 32, 16384, 128, w, n),
+    "fp8_vt": lambda t, c, sy, w, n: run_fp8(t, c, "fp8", sy.gaussian, 1, 32, 32768, 128, w, n, v_channel_major=True),
     "fp8_4k": lambda t, c, sy, w, n: run_fp8(t, c, "fp8", sy.gaussian, 1, 32, 4096, 128, w, n),
 }
 
@@ -451,6 +458,11 @@ def main():
             also[f"bf16_B1_H32_S{s}_d128"] = {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4)}
             r = run_fp8(torch, cfa, "fp8", synth.gaussian, 1, 32, s, 128, wb, sb)
             also[f"fp8_B1_H32_S{s}_d128"] = {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4)}
+        # V channel-major ([B, H, 128, S]): the same computation, operands read without transposes
+        r = run_fp8(torch, cfa, "fp8", synth.gaussian, 1, 32, 32768, 128, wb, sb, v_channel_major=True)
+        also["fp8_B1_H32_S32768_d128_v_channel_major"] = {
+            "tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4),
+            "pct_fp8_peak": round(100 * r["tflops"] / PEAK_TFLOPS["fp8"], 2)}
         r = run_fp8(torch, cfa, "mla", synth.gaussian, 1, 16, 32768, 192, wb, sb,
                     sustained_reps=0 if args.no_sustained else 1)
         also["mla_fp8_B1_H16_S32768_192_128"] = {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4),

@@ -10,6 +10,7 @@ Functions mirror the C entry points:
     attn_fwd_causal_bf16(q, k, v, softmax_scale=None)
     attn_fwd_causal_mla(q, k, v, q_descale, k_descale, v_descale, softmax_scale=None)
     attn_fwd_causal_fp8_ex(q, k, v, q_descale, k_descale, v_descale, softmax_scale=None, p_mode=None)
+    attn_fwd_causal_fp8_vt(q, k, vt, q_descale, k_descale, v_descale, softmax_scale=None, p_mode=None)
     attn_fwd_causal_bf16_ex(q, k, v, softmax_scale=None)
     quantize_e4m3(x) -> (codes, descale)      round_bf16(x) -> bf16 tensor
     key_mean(k) -> mean [B, H, D]             rotate_quantize_e4m3(x, signs, mean=None) -> (codes, descale)
@@ -65,6 +66,7 @@ def lib():
         L.attn_fwd_causal_bf16.argtypes = [P, P, P, P, P, F, I, I, I, I, I, P]
         SP = ctypes.POINTER(Strides)
         L.attn_fwd_causal_fp8_ex.argtypes = [P, P, P, P, P, F, F, F, F, I, I, I, I, I, I, SP, SP, SP, SP, I, P]
+        L.attn_fwd_causal_fp8_vt.argtypes = [P, P, P, P, P, F, F, F, F, I, I, I, I, I, I, SP, SP, SP, SP, I, P]
         L.attn_fwd_causal_bf16_ex.argtypes = [P, P, P, P, P, F, I, I, I, I, I, I, SP, SP, SP, SP, P]
         L.attn_quantize_e4m3.argtypes = [P, I64, P, P, P, P]
         L.attn_round_bf16.argtypes = [P, I64, P, P]
@@ -80,7 +82,7 @@ def lib():
         L.attn_status_string.argtypes = [I]
         L.attn_status_string.restype = ctypes.c_char_p
         for name in ("attn_fwd_causal_fp8", "attn_fwd_causal_mla", "attn_fwd_causal_fp8_debug",
-                     "attn_fwd_causal_bf16", "attn_fwd_causal_fp8_ex", "attn_fwd_causal_bf16_ex",
+                     "attn_fwd_causal_bf16", "attn_fwd_causal_fp8_ex", "attn_fwd_causal_fp8_vt", "attn_fwd_causal_bf16_ex",
                      "attn_quantize_e4m3", "attn_round_bf16", "attn_default_grid", "attn_key_mean",
                      "attn_rotate_quantize_e4m3", "attn_quantize_e4m3_static", "attn_rotate_quantize_e4m3_static"):
             getattr(L, name).restype = I
@@ -206,12 +208,15 @@ def _strides(t):
     return Strides(t.stride(0), t.stride(2), t.stride(1))
 
 
-def _ex_meta(q, k, v, out, lse):
+def _ex_meta(q, k, v, out, lse, v_channel_major=False):
     B, S, H, dqk = q.shape
     Bk, Sk, Hkv, dk = k.shape
-    if (Bk, Sk, dk) != (B, S, dqk) or tuple(v.shape[:3]) != (B, S, Hkv) or Hkv == 0 or H % Hkv:
+    if v.dim() != 4:
+        raise ValueError("v must be 4-D")
+    # v is [B, S, H_kv, d_v], or [B, H_kv, d_v, S] when channel-major
+    vB, vS, vH, dv = (v.shape[0], v.shape[3], v.shape[1], v.shape[2]) if v_channel_major else tuple(v.shape)
+    if (Bk, Sk, dk) != (B, S, dqk) or (vB, vS, vH) != (B, S, Hkv) or Hkv == 0 or H % Hkv:
         raise ValueError("q, k, v shapes disagree (k, v need H_kv heads with H a multiple of H_kv)")
-    dv = v.shape[3]
     if out is None:
         out = torch.empty((B, S, H, dv), dtype=torch.bfloat16, device=q.device)
     if lse is None:
@@ -221,7 +226,12 @@ def _ex_meta(q, k, v, out, lse):
     if tuple(out.shape) != (B, S, H, dv) or tuple(lse.shape) != (B, H, S) or not lse.is_contiguous():
         raise ValueError("out / lse shapes disagree (lse must be a dense [B, H, S] tensor)")
     _same_device(q, k, v, out, lse)
-    st = [_strides(t) for t in (q, k, v, out)]
+    if v_channel_major:
+        if not v.is_cuda or v.stride(3) != 1:
+            raise ValueError("vt must be a [B, H_kv, d_v, S] GPU view with contiguous keys")
+        st = [_strides(q), _strides(k), Strides(v.stride(0), v.stride(1), v.stride(2)), _strides(out)]
+    else:
+        st = [_strides(t) for t in (q, k, v, out)]
     return B, S, H, Hkv, dqk, dv, out, lse, st
 
 
@@ -238,6 +248,22 @@ def attn_fwd_causal_fp8_ex(q, k, v, q_descale, k_descale, v_descale, softmax_sca
                                       float(k_descale), float(v_descale), float(softmax_scale), B, H, Hkv, S, dqk,
                                       dv, *[ctypes.byref(x) for x in st], pm, _stream(q))
     _check("attn_fwd_causal_fp8_ex", rc)
+    return out, lse
+
+
+def attn_fwd_causal_fp8_vt(q, k, vt, q_descale, k_descale, v_descale, softmax_scale=None, p_mode=None,
+                           out=None, lse=None):
+    """attn_fwd_causal_fp8_ex with V channel-major: vt is a [B, H_kv, d_v, S] view with contiguous
+    keys (vt[b, g, d, s] = v[b, s, g, d]).  Results equal attn_fwd_causal_fp8_ex bit for bit."""
+    q, k, vt = _fp8_view(q), _fp8_view(k), _fp8_view(vt)
+    B, S, H, Hkv, dqk, dv, out, lse, st = _ex_meta(q, k, vt, out, lse, v_channel_major=True)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(dqk)
+    pm = P_DEFAULT if p_mode is None else int(p_mode)
+    rc = lib().attn_fwd_causal_fp8_vt(_ptr(q), _ptr(k), _ptr(vt), _ptr(out), _ptr(lse), float(q_descale),
+                                      float(k_descale), float(v_descale), float(softmax_scale), B, H, Hkv, S, dqk,
+                                      dv, *[ctypes.byref(x) for x in st], pm, _stream(q))
+    _check("attn_fwd_causal_fp8_vt", rc)
     return out, lse
 
 

@@ -28,6 +28,7 @@ struct Problem {
   float* lse;
   int B, H, Hkv, S, dqk, dv;
   attn_strides sq, sk, sv, so;
+  bool v_channel_major;  // v is [B][H_kv][d_v][S]: sv.seq is the channel row stride
 };
 
 attn_strides bshd(int S, int H, int d) {
@@ -65,7 +66,11 @@ int check_attn(const Problem& p, int elem) {
   int rc;
   if ((rc = check_tensor(p.sq, p.B, p.S, p.H, p.dqk, elem)) != ATTN_OK) return rc;
   if ((rc = check_tensor(p.sk, p.B, p.S, p.Hkv, p.dqk, elem)) != ATTN_OK) return rc;
-  if ((rc = check_tensor(p.sv, p.B, p.S, p.Hkv, p.dv, elem)) != ATTN_OK) return rc;
+  if (p.v_channel_major) {  // d_v rows of S contiguous keys: the same rules with rows and columns swapped
+    if ((rc = check_tensor(p.sv, p.B, p.dv, p.Hkv, p.S, elem)) != ATTN_OK) return rc;
+  } else if ((rc = check_tensor(p.sv, p.B, p.S, p.Hkv, p.dv, elem)) != ATTN_OK) {
+    return rc;
+  }
   if ((rc = check_tensor(p.so, p.B, p.S, p.H, p.dv, 2)) != ATTN_OK) return rc;
   return ATTN_OK;
 }
@@ -98,6 +103,7 @@ Problem make_problem(const void* q, const void* k, const void* v, void* out, flo
   p.sk = sk ? *sk : bshd(S, hk, dqk);
   p.sv = sv ? *sv : bshd(S, hk, dv);
   p.so = so ? *so : bshd(S, H, dv);
+  p.v_channel_major = false;
   return p;
 }
 
@@ -157,7 +163,8 @@ int run_fp8(const Problem& p, float qd, float kd, float vd, float sm, int p_mode
   a.dbg_o = dbg_o;
   a.dbg_codes = dbg_c;
   const bool exact = p_mode == ATTN_P_EXACT || (p_mode == ATTN_P_DEFAULT && p.dqk == 192);
-  const hipError_t e = cfa::launch_fp8(a, p.dqk, exact, debug, grid_for(p.B, p.H, p.S, ncu), (hipStream_t)stream);
+  const hipError_t e =
+      cfa::launch_fp8(a, p.dqk, exact, debug, p.v_channel_major, grid_for(p.B, p.H, p.S, ncu), (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -243,6 +250,25 @@ int attn_fwd_causal_fp8_ex(const void* q, const void* k, const void* v, void* ou
                            void* stream) {
   const Problem p = make_problem(q, k, v, out, lse, B, H, H_kv, S, d_qk, d_v, q_strides, k_strides, v_strides,
                                  out_strides);
+  return run_fp8(p, q_descale, k_descale, v_descale, softmax_scale, p_mode, nullptr, nullptr, false, stream);
+}
+
+int attn_fwd_causal_fp8_vt(const void* q, const void* k, const void* vt, void* out, float* lse, float q_descale,
+                           float k_descale, float v_descale, float softmax_scale, int B, int H, int H_kv, int S,
+                           int d_qk, int d_v, const attn_strides* q_strides, const attn_strides* k_strides,
+                           const attn_strides* vt_strides, const attn_strides* out_strides, int p_mode,
+                           void* stream) {
+  Problem p = make_problem(q, k, vt, out, lse, B, H, H_kv, S, d_qk, d_v, q_strides, k_strides, nullptr,
+                           out_strides);
+  if (vt_strides) {
+    p.sv = *vt_strides;
+  } else {  // dense [B][H_kv][d_v][S]
+    const int64_t hk = H_kv > 0 ? H_kv : 1;
+    p.sv.batch = hk * d_v * S;
+    p.sv.head = (int64_t)d_v * S;
+    p.sv.seq = S;
+  }
+  p.v_channel_major = true;
   return run_fp8(p, q_descale, k_descale, v_descale, softmax_scale, p_mode, nullptr, nullptr, false, stream);
 }
 

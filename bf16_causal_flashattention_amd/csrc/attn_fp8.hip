@@ -76,8 +76,15 @@ __host__ __device__ constexpr int v_key_of_row(int r) {
   return 32 * (r >> 5) + 8 * ((r & 7) >> 1) + ((r & 31) >> 3) + 4 * (r & 1);
 }
 __host__ __device__ constexpr int v_row_offset(int r) { return 128 * r + 16 * (r >> 2); }
+// Key-contiguous V (V^T rows: one row of S key bytes per channel d): the slot holds the 128
+// channels as rows of 8 data cells and one pad cell (144 bytes, the K row pitch), so a PV
+// operand is one 32-byte read per lane, conflict-free like the K reads.  Within each 64-key
+// scale block the four 16-key cells are stored in the order 0, 2, 1, 3, so that lane half hh
+// finds its keys 16 hh + 0..15 and 32 + 16 hh + 0..15 (the key order of the P operand)
+// together at byte 32 hh of the block.
+__host__ __device__ constexpr int vt_cell_src(int c) { return (c & 4) | ((c & 1) << 1) | ((c >> 1) & 1); }
 
-template <int DQK>
+template <int DQK, bool VT = false>
 struct Fp8Lds {
   static constexpr int kKCols = DQK / 16;
   static constexpr int kKSpr = kKCols + 1;  // cells per K row
@@ -85,7 +92,9 @@ struct Fp8Lds {
   static constexpr int kKCells = 128 * kKSpr;
   static constexpr int kKSlot = 16 * kKCells;
   static constexpr int kVGroupCells = 33;  // 4 rows of 8 cells + 1 pad cell
-  static constexpr int kVCells = 1088;     // 32 groups + 32 spare cells (a whole last DMA instruction)
+  static constexpr int kVtSpr = 9;         // key-contiguous V: cells per channel row
+  // 32 groups + 32 spare cells (a whole last DMA instruction); or 128 channel rows
+  static constexpr int kVCells = VT ? 128 * kVtSpr : 1088;
   static constexpr int kVSlot = 16 * kVCells;
   // byte offsets of the transpose reads (see v_row_of_key): the 64 keys of scale block n start
   // 8448 n bytes in; the four 8-key pieces of a lane half at keys +0, +8, +32, +40 lie 0, 256,
@@ -116,9 +125,9 @@ constexpr int kStgPitch = 272;
 constexpr int kStgWave = kWaveRows * kStgPitch;
 static_assert(kThreads / 64 * kStgWave <= Fp8Lds<128>::kBytes, "O staging exceeds the LDS of the kernel");
 
-template <int DQK, bool EXACT_P, bool DEBUG>
+template <int DQK, bool EXACT_P, bool DEBUG, bool VT>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
-  using L = Fp8Lds<DQK>;
+  using L = Fp8Lds<DQK, VT>;
   constexpr int KC = DQK / 64;
   __shared__ __attribute__((aligned(16))) uint8_t smem[L::kBytes];
 
@@ -130,7 +139,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
   const Schedule sch = make_schedule(a.B, H, S);
   const ItemRange work = xcd_items(blockIdx.x, gridDim.x, sch.items);
 
-  const int krs = a.mk.ss, vrs = a.mv.ss;  // key / value row strides in bytes
+  // key row stride in bytes; value row stride (key-major V) or channel row stride (VT)
+  const int krs = a.mk.ss, vrs = a.mv.ss;
 
   // per-lane LDS read bases
   const int k_rd = l32 * L::kKStride + 32 * hh;
@@ -159,6 +169,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
     if (stage_k) {
       const int row = (cell / L::kKSpr) & 127, col = cell % L::kKSpr;
       st_goff[p] = ((row & ~31) | key_perm_fp8(row & 31)) * krs + 16 * (col < L::kKCols ? col : 0);
+    } else if constexpr (VT) {  // pad cells copy the row's first 16 bytes
+      const int row = (cell / L::kVtSpr) & 127, col = cell % L::kVtSpr;
+      st_goff[p] = row * vrs + 16 * (col < 8 ? vt_cell_src(col) : 0);
     } else {  // pad and spare cells copy the block's first 16 bytes
       const int g = cell / L::kVGroupCells, w = cell % L::kVGroupCells;
       const bool data = g < 32 && w < 32;
@@ -183,7 +196,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
     const int hk = h / a.G;  // key/value head of query head h
     const uint8_t* qbh = a.q + b * a.mq.sb + h * a.mq.sh;
     const uint8_t* st_head = stage_k ? a.k + b * a.mk.sb + hk * a.mk.sh : a.v + b * a.mv.sb + hk * a.mv.sh;
-    const int st_rs = stage_k ? krs : vrs;
+    // bytes from one 128-key block to the next in the staged tensor
+    const int64_t st_bstep = stage_k || !VT ? (int64_t)kBlockKeys * (stage_k ? krs : vrs) : kBlockKeys;
 
     for (int pass = 0; pass < 2; ++pass) {
       // the long tile of the pair first: the workgroups of one XCD then start on key block 0
@@ -196,7 +210,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
 
       // DMA of block blk: K by group 0 into slot blk % 2, V by group 1 into slot blk % 3
       auto stage = [&](int blk) {
-        const uint8_t* src = st_head + (int64_t)(blk * kBlockKeys) * st_rs;
+        const uint8_t* src = st_head + blk * st_bstep;
         uint8_t* dst = smem + st_lds + (stage_k ? (blk & 1) * L::kKSlot : (blk % 3) * L::kVSlot);
 #pragma unroll
         for (int p = 0; p < NR; ++p)
@@ -255,11 +269,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
       };
-      // O^T += V^T P^T with the 2^-o operand scale; V^T by transpose reads (4 per MFMA)
+      // O^T += V^T P^T with the 2^-o operand scale; V^T by transpose reads (4 per MFMA), or
+      // for key-contiguous V one 32-byte read per MFMA
       auto pv = [&](int blk) {
         const uint8_t* sv = smem + (blk % 3) * L::kVSlot + v_tr;
+        const uint8_t* svt = smem + L::kVBase + (blk % 3) * L::kVSlot + l32 * (16 * L::kVtSpr) + 32 * hh;
         auto vread = [&](int t) {
           const int n = t / 4, dt = t % 4;
+          if constexpr (VT) return *(const v8i*)(svt + 32 * dt * (16 * L::kVtSpr) + 64 * n);
           const uint8_t* p = sv + L::kVHalf * n + 32 * dt;
           const v2i r0 = lds_tr8(p);
           const v2i r1 = lds_tr8(p + L::kVPc8);
@@ -277,11 +294,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
                                                                       127 - o_cur[n]);
         }
         if constexpr (DQK == 128) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+          constexpr int R = VT ? 2 : 4;  // LDS read instructions per operand
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * R, 1);
 #pragma unroll
           for (int t = 0; t < 7; ++t) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, R, 1);
           }
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
         }
@@ -461,23 +479,33 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
 
 }  // namespace
 
-hipError_t launch_fp8(const Fp8Args& a, int dqk, bool exact_p, bool debug, int grid, hipStream_t stream) {
-  const dim3 g(grid), t(kThreads);
-  if (debug) {  // the test hook runs the default P mode of each head dimension
-    if (dqk == 128)
-      hipLaunchKernelGGL((attn_fwd_fp8_kernel<128, false, true>), g, t, 0, stream, a);
-    else
-      hipLaunchKernelGGL((attn_fwd_fp8_kernel<192, true, true>), g, t, 0, stream, a);
-  } else if (dqk == 128) {
+template <bool VT>
+void launch_fp8_layout(const Fp8Args& a, int dqk, bool exact_p, dim3 g, dim3 t, hipStream_t stream) {
+  if (dqk == 128) {
     if (exact_p)
-      hipLaunchKernelGGL((attn_fwd_fp8_kernel<128, true, false>), g, t, 0, stream, a);
+      hipLaunchKernelGGL((attn_fwd_fp8_kernel<128, true, false, VT>), g, t, 0, stream, a);
     else
-      hipLaunchKernelGGL((attn_fwd_fp8_kernel<128, false, false>), g, t, 0, stream, a);
+      hipLaunchKernelGGL((attn_fwd_fp8_kernel<128, false, false, VT>), g, t, 0, stream, a);
   } else {
     if (exact_p)
-      hipLaunchKernelGGL((attn_fwd_fp8_kernel<192, true, false>), g, t, 0, stream, a);
+      hipLaunchKernelGGL((attn_fwd_fp8_kernel<192, true, false, VT>), g, t, 0, stream, a);
     else
-      hipLaunchKernelGGL((attn_fwd_fp8_kernel<192, false, false>), g, t, 0, stream, a);
+      hipLaunchKernelGGL((attn_fwd_fp8_kernel<192, false, false, VT>), g, t, 0, stream, a);
+  }
+}
+
+hipError_t launch_fp8(const Fp8Args& a, int dqk, bool exact_p, bool debug, bool v_channel_major, int grid,
+                      hipStream_t stream) {
+  const dim3 g(grid), t(kThreads);
+  if (debug) {  // the test hook runs the default P mode of each head dimension, key-major V
+    if (dqk == 128)
+      hipLaunchKernelGGL((attn_fwd_fp8_kernel<128, false, true, false>), g, t, 0, stream, a);
+    else
+      hipLaunchKernelGGL((attn_fwd_fp8_kernel<192, true, true, false>), g, t, 0, stream, a);
+  } else if (v_channel_major) {
+    launch_fp8_layout<true>(a, dqk, exact_p, g, t, stream);
+  } else {
+    launch_fp8_layout<false>(a, dqk, exact_p, g, t, stream);
   }
   return hipGetLastError();
 }

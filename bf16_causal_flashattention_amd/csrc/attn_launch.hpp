@@ -16,7 +16,8 @@ struct TensorMap {
 struct Fp8Args {
   const uint8_t* q;  // e4m3 codes, [B][S][H][d_qk] through mq
   const uint8_t* k;  // e4m3 codes, [B][S][H_kv][d_qk] through mk
-  const uint8_t* v;  // e4m3 codes, [B][S][H_kv][128] through mv
+  const uint8_t* v;  // e4m3 codes, [B][S][H_kv][128] through mv; channel-major V: [B][H_kv][128][S]
+                     // with mv.ss the stride between channel rows (keys contiguous)
   uint16_t* out;     // bf16 bits, [B][S][H][128] through mo
   float* lse;        // [B][H][S] (contiguous) or null
   float cp;          // fp32(softmax_scale * q_descale * k_descale * log2 e)
@@ -40,7 +41,8 @@ struct Bf16Args {
   TensorMap mq, mk, mv, mo;
 };
 
-hipError_t launch_fp8(const Fp8Args& a, int dqk, bool exact_p, bool debug, int grid, hipStream_t stream);
+hipError_t launch_fp8(const Fp8Args& a, int dqk, bool exact_p, bool debug, bool v_channel_major, int grid,
+                      hipStream_t stream);
 hipError_t launch_bf16(const Bf16Args& a, int dqk, int grid, hipStream_t stream);
 hipError_t launch_quantize_e4m3(const float* x, int64_t n, uint8_t* codes, float* descale, uint32_t* ws,
                                 hipStream_t stream);

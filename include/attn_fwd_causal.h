@@ -112,6 +112,20 @@ int attn_fwd_causal_fp8_ex(const void* q, const void* k, const void* v, void* ou
                            const attn_strides* v_strides, const attn_strides* out_strides, int p_mode,
                            void* stream);
 
+/* attn_fwd_causal_fp8_ex with V given channel-major: vt holds, per batch and key/value
+ * head, d_v = 128 rows of S contiguous e4m3 key codes (vt[b][g][d][s] = v[b][s][g][d]),
+ * the layout in which the PV product (paper Sec. IV-A, O^T = V^T P^T) reads its operand
+ * directly.  vt_strides: batch, head and, in its seq field, the stride between channel
+ * rows, in bytes (NULL = dense [B][H_kv][128][S]); the same rules as the other strides
+ * (multiples of 16 bytes, non-negative, offsets below 2^31).  Results are bit-identical
+ * to attn_fwd_causal_fp8_ex on the same values.  Other arguments and errors as for
+ * attn_fwd_causal_fp8_ex. */
+int attn_fwd_causal_fp8_vt(const void* q, const void* k, const void* vt, void* out, float* lse, float q_descale,
+                           float k_descale, float v_descale, float softmax_scale, int B, int H, int H_kv, int S,
+                           int d_qk, int d_v, const attn_strides* q_strides, const attn_strides* k_strides,
+                           const attn_strides* vt_strides, const attn_strides* out_strides, int p_mode,
+                           void* stream);
+
 /* General BF16 entry point: d_qk = 128, or the MLA shape d_qk = 192, with d_v = 128;
  * grouped-query heads and strides as for attn_fwd_causal_fp8_ex (strides in bf16
  * elements).  At d_qk = 192 the lazy-rescale threshold is 8 binades, as in the paper's

@@ -97,6 +97,16 @@ def _fp8_ex(**kw):
                                             a["sk"], a["sv"], a["so"], a["pm"], None)
 
 
+def _fp8_vt(**kw):
+    # channel-major V: the v strides are (batch, head, channel row), keys contiguous
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, qd=1.0, kd=1.0, vd=1.0, sm=0.1, B=1, H=4, Hkv=2, S=256,
+             dqk=128, dv=128, sq=None, sk=None, sv=None, so=None, pm=-1)
+    a.update(kw)
+    return cfa.lib().attn_fwd_causal_fp8_vt(a["q"], a["k"], a["v"], a["out"], a["lse"], a["qd"], a["kd"], a["vd"],
+                                            a["sm"], a["B"], a["H"], a["Hkv"], a["S"], a["dqk"], a["dv"], a["sq"],
+                                            a["sk"], a["sv"], a["so"], a["pm"], None)
+
+
 def _bf16_ex(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, sm=0.1, B=1, H=4, Hkv=2, S=256, dqk=128, dv=128,
              sq=None, sk=None, sv=None, so=None)
@@ -106,7 +116,7 @@ def _bf16_ex(**kw):
                                              a["so"], None)
 
 
-@pytest.mark.parametrize("call", [_fp8_ex, _bf16_ex])
+@pytest.mark.parametrize("call", [_fp8_ex, _fp8_vt, _bf16_ex])
 def test_ex_validation_errors(call):
     assert call(q=None) == -1
     assert call(Hkv=3) == -2             # H_kv must divide H
@@ -120,6 +130,15 @@ def test_ex_validation_errors(call):
     assert call(sv=_st(1 << 20, 1 << 27, 1 << 24)) == -4     # 128 rows of the seq stride beyond 2^31 bytes
     assert call(B=0, q=None, k=None, v=None, out=None) == 0  # empty problem
     assert call(sm=0.0) == -5
+
+
+def test_vt_strides_checked_channel_major():
+    # the channel-major V tensor is [B][H_kv][128][S]: its third stride steps between channel rows
+    assert _fp8_vt(sv=_st(2 * 128 * 256, 128 * 256, 40)) == -3        # channel stride not 16-byte aligned
+    assert _fp8_vt(sv=_st(0, 3 << 29, 1 << 23)) == -4                 # last channel row beyond 2^31
+    assert _fp8_vt(S=1 << 17, H=2, Hkv=2, sv=_st(0, 1 << 30, 1 << 24)) == -4  # 128 channel rows beyond 2^31
+    assert _fp8_vt(pm=2) == -5
+    assert _fp8_vt(dqk=64) == -2
 
 
 def test_ex_p_mode_and_head_dims():
@@ -261,6 +280,8 @@ def test_binding_rejects_host_tensors_before_any_call():
         cfa.attn_fwd_causal_fp8_ex(q, q, q, 1.0, 1.0, 1.0)
     with pytest.raises((ValueError, TypeError)):
         cfa.attn_fwd_causal_fp8(q, q, q, 1.0, 1.0, 1.0)
+    with pytest.raises((ValueError, TypeError)):
+        cfa.attn_fwd_causal_fp8_vt(q, q, q.view(1, 1, 128, 256), 1.0, 1.0, 1.0)
     b = torch.zeros((1, 256, 1, 128), dtype=torch.bfloat16)
     with pytest.raises((ValueError, TypeError)):
         cfa.attn_fwd_causal_bf16_ex(b, b, b)

@@ -102,7 +102,13 @@ def test_fp8_ex(B, H, Hkv, S, dqk, p_mode, layout):
     assert torch.equal(out.contiguous().view(torch.int16), ref_out.view(torch.int16))
     assert torch.equal(lse, ref_lse)
 
-    # against the oracle on expanded heads
+    _check_fp8_oracle(out.contiguous(), lse, qc, kc, vc, G, dq, dk, dv, c, exact_p, B, H, S)
+
+
+def _check_fp8_oracle(out, lse, qc, kc, vc, G, dq, dk, dv, c, exact_p, B, H, S, strict=True):
+    """out (BSHD) and lse against the oracle, with k/v codes expanded to H heads.  strict adds
+    the element-wise max-abs gate against the emulation (see test_fp8_vt for when it is not a
+    bound)."""
     kcE, vcE = np.repeat(kc, G, axis=2), np.repeat(vc, G, axis=2)
     scheme = oracle.Fp8Scheme(exact_p=exact_p)
     groups = all_groups(B, H, S)
@@ -114,9 +120,71 @@ def test_fp8_ex(B, H, Hkv, S, dqk, p_mode, layout):
            "fp64_rms": rms_rel(got, ex), "lse_emu": float(np.max(np.abs(glse - emu["lse"]))),
            "lse_fp64": float(np.max(np.abs(glse - ex_lse)))}
     print("RESULT", res, flush=True)
-    assert res["emu_maxabs"] <= TOL_EMU_MAXABS and res["emu_rms"] <= TOL_EMU_RMS, res
+    assert res["emu_maxabs"] <= TOL_EMU_MAXABS or not strict, res
+    assert res["emu_rms"] <= TOL_EMU_RMS, res
     assert res["fp64_rms"] <= TOL_FP64_RMS_FP8, res
     assert res["lse_emu"] <= LSE_EMU_NATS and res["lse_fp64"] <= LSE_FP64_NATS, res
+
+
+def _channel_major(vg, padded):
+    """[B, H_kv, 128, S] view of the key-major codes vg [B, S, H_kv, 128] (uint8); with
+    padded, each channel row sits in a row of S + 256 bytes, 128 bytes in."""
+    vt = vg.permute(0, 2, 3, 1).contiguous()
+    if not padded:
+        return vt
+    B, Hkv, d, S = vt.shape
+    buf = torch.zeros((B, Hkv, d, S + 256), dtype=torch.uint8, device=DEV)
+    buf[..., 128:128 + S] = vt
+    return buf[..., 128:128 + S]
+
+
+@pytest.mark.parametrize("B,H,Hkv,S,dqk,p_mode,padded", [
+    (2, 4, 2, 768, 128, None, False),      # GQA G=2, odd tile count
+    (1, 4, 4, 1024, 128, None, True),      # MHA, padded channel rows
+    (2, 4, 2, 512, 192, None, True),       # MLA shape, exact P
+    (1, 2, 2, 1024, 128, cfa.P_EXACT, False),
+    (1, 2, 1, 768, 192, cfa.P_LEAN, False),
+    (1, 1, 1, 256, 128, None, False),      # a single tile
+])
+def test_fp8_vt(B, H, Hkv, S, dqk, p_mode, padded):
+    """Channel-major V: identical bit for bit to the key-major entry point, and within the
+    oracle's RMS and LSE bounds.  The element-wise max-abs gate is left out: a probability code
+    whose exact value lies within the FP8 MFMA's score-error band of a rounding boundary may
+    round either way (test_debug_codes_and_exponents checks that codes differ only there), and
+    in a row of few keys one such code moves O by more than that gate (measured: 0.026 in a
+    24-key row of the 512-key MLA case)."""
+    _case("fp8_vt", B, H, Hkv, S, dqk, p_mode, padded)
+    G = H // Hkv
+    q, k, v = _inputs(B, H, Hkv, S, dqk, seed=5 * S + H + dqk)
+    gq = [cfa.quantize_e4m3(torch.from_numpy(x).to(DEV)) for x in (q, k, v)]
+    (qg, dq), (kg, dk), (vg, dv) = [(c_.view(torch.uint8), float(d_.item())) for c_, d_ in gq]
+    c = 1.0 / math.sqrt(dqk)
+    vt = _channel_major(vg, padded)
+    out, lse = cfa.attn_fwd_causal_fp8_vt(qg, kg, vt, dq, dk, dv, softmax_scale=c, p_mode=p_mode)
+    ref_out, ref_lse = cfa.attn_fwd_causal_fp8_ex(qg, kg, vg, dq, dk, dv, softmax_scale=c, p_mode=p_mode)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)) and torch.equal(lse, ref_lse)
+    (qc, _), (kc, _), (vc, _) = [oracle.quantize_e4m3(x) for x in (q, k, v)]
+    exact_p = (p_mode == cfa.P_EXACT) or (p_mode is None and dqk == 192)
+    _check_fp8_oracle(out, lse, qc, kc, vc, G, dq, dk, dv, c, exact_p, B, H, S, strict=False)
+
+
+@pytest.mark.parametrize("H,Hkv,dqk", [(32, 32, 128), (32, 8, 128), (16, 16, 192)])
+def test_fp8_vt_full_size_bitwise(H, Hkv, dqk):
+    """At S = 32768 (the paper's long-sequence shapes): channel-major V equals key-major V bit
+    for bit, over every output."""
+    B, S = 1, 32768
+    _case("fp8_vt full size", B, H, Hkv, S, dqk)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(1000 + H + Hkv + dqk)
+    q, k, v = (torch.randn((B, S, h, d), generator=g, device=DEV).mul_(16).to(torch.float8_e4m3fn)
+               .view(torch.uint8) for h, d in ((H, dqk), (Hkv, dqk), (Hkv, 128)))
+    vt = v.permute(0, 2, 3, 1).contiguous()
+    o1, l1 = cfa.attn_fwd_causal_fp8_ex(q, k, v, 1 / 16, 1 / 16, 1 / 16)
+    o2, l2 = cfa.attn_fwd_causal_fp8_vt(q, k, vt, 1 / 16, 1 / 16, 1 / 16)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o1.float()).any()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
 
 
 def test_fp8_ex_matches_basic_entry_points():
