@@ -65,6 +65,8 @@ def lib():
         L.attn_fwd_causal_fp8_debug.argtypes = [P, P, P, P, P, F, F, F, F, I, I, I, I, I, P, P, P]
         L.attn_fwd_causal_bf16.argtypes = [P, P, P, P, P, F, I, I, I, I, I, P]
         SP = ctypes.POINTER(Strides)
+        L.attn_fwd_causal_fp8_debug_ex.argtypes = [P, P, P, P, P, F, F, F, F, I, I, I, I, I, I, SP, SP, SP, SP, I,
+                                                   P, P, P, P]
         L.attn_fwd_causal_fp8_ex.argtypes = [P, P, P, P, P, F, F, F, F, I, I, I, I, I, I, SP, SP, SP, SP, I, P]
         L.attn_fwd_causal_fp8_vt.argtypes = [P, P, P, P, P, F, F, F, F, I, I, I, I, I, I, SP, SP, SP, SP, I, P]
         L.attn_fwd_causal_bf16_ex.argtypes = [P, P, P, P, P, F, I, I, I, I, I, I, SP, SP, SP, SP, P]
@@ -82,6 +84,7 @@ def lib():
         L.attn_status_string.argtypes = [I]
         L.attn_status_string.restype = ctypes.c_char_p
         for name in ("attn_fwd_causal_fp8", "attn_fwd_causal_mla", "attn_fwd_causal_fp8_debug",
+                     "attn_fwd_causal_fp8_debug_ex",
                      "attn_fwd_causal_bf16", "attn_fwd_causal_fp8_ex", "attn_fwd_causal_fp8_vt", "attn_fwd_causal_bf16_ex",
                      "attn_quantize_e4m3", "attn_round_bf16", "attn_default_grid", "attn_key_mean",
                      "attn_rotate_quantize_e4m3", "attn_quantize_e4m3_static", "attn_rotate_quantize_e4m3_static"):
@@ -182,6 +185,27 @@ def attn_fwd_causal_fp8_debug(q, k, v, q_descale, k_descale, v_descale, softmax_
     out, lse = _fp8_call("attn_fwd_causal_fp8_debug", q, k, v, q_descale, k_descale, v_descale, softmax_scale,
                          None, None, debug=(dbg_o, dbg_c))
     return out, lse, dbg_o, dbg_c
+
+
+def attn_fwd_causal_fp8_debug_ex(q, k, v, q_descale, k_descale, v_descale, softmax_scale=None, p_mode=None):
+    """Test hook: attn_fwd_causal_fp8_ex (key-major V) that also returns the per-(row, 64-key block)
+    scale exponents (255 where untouched), the probability codes (0 where untouched) and the raw
+    fp32 scores the score MFMA produced, before the causal mask (NaN where untouched); the last
+    three are [B*H*S, S/64] and [B*H*S, S] with row (b*H + h)*S + i."""
+    q, k, v = _fp8_view(q), _fp8_view(k), _fp8_view(v)
+    B, S, H, Hkv, dqk, dv, out, lse, st = _ex_meta(q, k, v, None, None)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(dqk)
+    pm = P_DEFAULT if p_mode is None else int(p_mode)
+    dbg_o = torch.full((B * H * S, S // 64), 255, dtype=torch.uint8, device=q.device)
+    dbg_c = torch.zeros((B * H * S, S), dtype=torch.uint8, device=q.device)
+    dbg_s = torch.full((B * H * S, S), float("nan"), dtype=torch.float32, device=q.device)
+    rc = lib().attn_fwd_causal_fp8_debug_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), float(q_descale),
+                                            float(k_descale), float(v_descale), float(softmax_scale), B, H, Hkv, S,
+                                            dqk, dv, *[ctypes.byref(x) for x in st], pm, _ptr(dbg_o), _ptr(dbg_c),
+                                            _ptr(dbg_s), _stream(q))
+    _check("attn_fwd_causal_fp8_debug_ex", rc)
+    return out, lse, dbg_o, dbg_c, dbg_s
 
 
 def attn_fwd_causal_bf16(q, k, v, softmax_scale=None, out=None, lse=None):

@@ -51,6 +51,30 @@ int check_tensor(const attn_strides& t, int B, int S, int heads, int d, int elem
   return ATTN_OK;
 }
 
+// The output's (b, h, s) rows must not overlap, or several workgroups would write the same
+// bytes.  Sufficient test: with the levels of extent > 1 sorted by stride, each stride is at
+// least the span that the levels below it cover (d elements to begin with).  Rejects zero
+// strides (expanded views) and interleaved rows.
+int check_no_overlap(const attn_strides& t, int B, int S, int heads, int d) {
+  int64_t st[3] = {t.batch, t.head, t.seq}, n[3] = {B, heads, S};
+  for (int i = 0; i < 3; ++i)  // sort the three levels by stride
+    for (int j = i + 1; j < 3; ++j)
+      if (st[j] < st[i]) {
+        const int64_t a = st[i], c = n[i];
+        st[i] = st[j];
+        n[i] = n[j];
+        st[j] = a;
+        n[j] = c;
+      }
+  int64_t span = d;
+  for (int i = 0; i < 3; ++i) {
+    if (n[i] <= 1) continue;
+    if (st[i] < span) return ATTN_ERR_ARG;
+    span += (n[i] - 1) * st[i];
+  }
+  return ATTN_OK;
+}
+
 // common checks of the attention entry points; returns ATTN_OK, 1 for an empty problem,
 // or an error
 int check_attn(const Problem& p, int elem) {
@@ -72,6 +96,7 @@ int check_attn(const Problem& p, int elem) {
     return rc;
   }
   if ((rc = check_tensor(p.so, p.B, p.S, p.H, p.dv, 2)) != ATTN_OK) return rc;
+  if ((rc = check_no_overlap(p.so, p.B, p.S, p.H, p.dv)) != ATTN_OK) return rc;
   return ATTN_OK;
 }
 
@@ -128,7 +153,7 @@ int grid_for(int B, int H, int S, int num_cu) {
 }
 
 int run_fp8(const Problem& p, float qd, float kd, float vd, float sm, int p_mode, uint8_t* dbg_o, uint8_t* dbg_c,
-            bool debug, void* stream) {
+            float* dbg_s, bool debug, void* stream) {
   if (p.dqk != 128 && p.dqk != 192) return ATTN_ERR_SHAPE;
   if (p.dv != 128) return ATTN_ERR_SHAPE;
   if (p_mode != ATTN_P_DEFAULT && p_mode != ATTN_P_LEAN && p_mode != ATTN_P_EXACT) return ATTN_ERR_ARG;
@@ -139,6 +164,7 @@ int run_fp8(const Problem& p, float qd, float kd, float vd, float sm, int p_mode
   if (debug) {
     if (!dbg_o || !dbg_c) return ATTN_ERR_NULL;
     if ((int64_t)p.B * p.H * p.S * p.S > (INT64_C(1) << 28)) return ATTN_ERR_RANGE;
+    if (dbg_s && !aligned(dbg_s, 16)) return ATTN_ERR_ALIGN;
   }
   const float cp = (float)((double)sm * (double)qd * (double)kd * kLog2e);
   if (!isfinite(cp) || !(cp > 0.0f)) return ATTN_ERR_ARG;
@@ -162,6 +188,7 @@ int run_fp8(const Problem& p, float qd, float kd, float vd, float sm, int p_mode
   a.mo = tmap(p.so, 2);
   a.dbg_o = dbg_o;
   a.dbg_codes = dbg_c;
+  a.dbg_scores = dbg_s;
   const bool exact = p_mode == ATTN_P_EXACT || (p_mode == ATTN_P_DEFAULT && p.dqk == 192);
   const hipError_t e =
       cfa::launch_fp8(a, p.dqk, exact, debug, p.v_channel_major, grid_for(p.B, p.H, p.S, ncu), (hipStream_t)stream);
@@ -232,7 +259,8 @@ int attn_fwd_causal_fp8(const void* q, const void* k, const void* v, void* out, 
                         int d_v, void* stream) {
   if (d_qk != 128) return ATTN_ERR_SHAPE;
   const Problem p = make_problem(q, k, v, out, lse, B, H, H, S, d_qk, d_v, nullptr, nullptr, nullptr, nullptr);
-  return run_fp8(p, q_descale, k_descale, v_descale, softmax_scale, ATTN_P_LEAN, nullptr, nullptr, false, stream);
+  return run_fp8(p, q_descale, k_descale, v_descale, softmax_scale, ATTN_P_LEAN, nullptr, nullptr, nullptr, false,
+                 stream);
 }
 
 int attn_fwd_causal_mla(const void* q, const void* k, const void* v, void* out, float* lse, float q_descale,
@@ -240,7 +268,8 @@ int attn_fwd_causal_mla(const void* q, const void* k, const void* v, void* out, 
                         int d_v, void* stream) {
   if (d_qk != 192) return ATTN_ERR_SHAPE;
   const Problem p = make_problem(q, k, v, out, lse, B, H, H, S, d_qk, d_v, nullptr, nullptr, nullptr, nullptr);
-  return run_fp8(p, q_descale, k_descale, v_descale, softmax_scale, ATTN_P_EXACT, nullptr, nullptr, false, stream);
+  return run_fp8(p, q_descale, k_descale, v_descale, softmax_scale, ATTN_P_EXACT, nullptr, nullptr, nullptr, false,
+                 stream);
 }
 
 int attn_fwd_causal_fp8_ex(const void* q, const void* k, const void* v, void* out, float* lse, float q_descale,
@@ -250,7 +279,8 @@ int attn_fwd_causal_fp8_ex(const void* q, const void* k, const void* v, void* ou
                            void* stream) {
   const Problem p = make_problem(q, k, v, out, lse, B, H, H_kv, S, d_qk, d_v, q_strides, k_strides, v_strides,
                                  out_strides);
-  return run_fp8(p, q_descale, k_descale, v_descale, softmax_scale, p_mode, nullptr, nullptr, false, stream);
+  return run_fp8(p, q_descale, k_descale, v_descale, softmax_scale, p_mode, nullptr, nullptr, nullptr, false,
+                 stream);
 }
 
 int attn_fwd_causal_fp8_vt(const void* q, const void* k, const void* vt, void* out, float* lse, float q_descale,
@@ -269,7 +299,8 @@ int attn_fwd_causal_fp8_vt(const void* q, const void* k, const void* vt, void* o
     p.sv.seq = S;
   }
   p.v_channel_major = true;
-  return run_fp8(p, q_descale, k_descale, v_descale, softmax_scale, p_mode, nullptr, nullptr, false, stream);
+  return run_fp8(p, q_descale, k_descale, v_descale, softmax_scale, p_mode, nullptr, nullptr, nullptr, false,
+                 stream);
 }
 
 int attn_fwd_causal_fp8_debug(const void* q, const void* k, const void* v, void* out, float* lse,
@@ -277,7 +308,19 @@ int attn_fwd_causal_fp8_debug(const void* q, const void* k, const void* v, void*
                               int H, int S, int d_qk, int d_v, uint8_t* dbg_o, uint8_t* dbg_codes,
                               void* stream) {
   const Problem p = make_problem(q, k, v, out, lse, B, H, H, S, d_qk, d_v, nullptr, nullptr, nullptr, nullptr);
-  return run_fp8(p, q_descale, k_descale, v_descale, softmax_scale, ATTN_P_DEFAULT, dbg_o, dbg_codes, true,
+  return run_fp8(p, q_descale, k_descale, v_descale, softmax_scale, ATTN_P_DEFAULT, dbg_o, dbg_codes, nullptr,
+                 true, stream);
+}
+
+int attn_fwd_causal_fp8_debug_ex(const void* q, const void* k, const void* v, void* out, float* lse,
+                                 float q_descale, float k_descale, float v_descale, float softmax_scale, int B,
+                                 int H, int H_kv, int S, int d_qk, int d_v, const attn_strides* q_strides,
+                                 const attn_strides* k_strides, const attn_strides* v_strides,
+                                 const attn_strides* out_strides, int p_mode, uint8_t* dbg_o, uint8_t* dbg_codes,
+                                 float* dbg_scores, void* stream) {
+  const Problem p = make_problem(q, k, v, out, lse, B, H, H_kv, S, d_qk, d_v, q_strides, k_strides, v_strides,
+                                 out_strides);
+  return run_fp8(p, q_descale, k_descale, v_descale, softmax_scale, p_mode, dbg_o, dbg_codes, dbg_scores, true,
                  stream);
 }
 

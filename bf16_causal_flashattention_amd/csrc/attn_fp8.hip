@@ -308,6 +308,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
       // rare rescale of O and l happens here, in the softmax phase), exponents o for blk
       auto max_step = [&](int blk, bool first) {
         const int key0 = blk * kBlockKeys;
+        if constexpr (DEBUG) {  // raw scores as the MFMA left them, before the mask
+          if (a.dbg_scores != nullptr) {
+            float* srow = a.dbg_scores + ((int64_t)(b * H + h) * S + qrow) * S + key0 + 16 * hh;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+              for (int r = 0; r < 16; r += 4)
+                *(v4f*)(srow + 32 * u + r) = (v4f){sacc[u][r], sacc[u][r + 1], sacc[u][r + 2], sacc[u][r + 3]};
+          }
+        }
         if (key0 + kBlockKeys - 1 > row0) {  // diagonal block: key key0+32u+16hh+r
 #pragma unroll
           for (int u = 0; u < 4; ++u)
@@ -497,11 +507,18 @@ void launch_fp8_layout(const Fp8Args& a, int dqk, bool exact_p, dim3 g, dim3 t, 
 hipError_t launch_fp8(const Fp8Args& a, int dqk, bool exact_p, bool debug, bool v_channel_major, int grid,
                       hipStream_t stream) {
   const dim3 g(grid), t(kThreads);
-  if (debug) {  // the test hook runs the default P mode of each head dimension, key-major V
-    if (dqk == 128)
-      hipLaunchKernelGGL((attn_fwd_fp8_kernel<128, false, true, false>), g, t, 0, stream, a);
-    else
-      hipLaunchKernelGGL((attn_fwd_fp8_kernel<192, true, true, false>), g, t, 0, stream, a);
+  if (debug) {  // the test hooks: either P mode at either head dimension, key-major V
+    if (dqk == 128) {
+      if (exact_p)
+        hipLaunchKernelGGL((attn_fwd_fp8_kernel<128, true, true, false>), g, t, 0, stream, a);
+      else
+        hipLaunchKernelGGL((attn_fwd_fp8_kernel<128, false, true, false>), g, t, 0, stream, a);
+    } else {
+      if (exact_p)
+        hipLaunchKernelGGL((attn_fwd_fp8_kernel<192, true, true, false>), g, t, 0, stream, a);
+      else
+        hipLaunchKernelGGL((attn_fwd_fp8_kernel<192, false, true, false>), g, t, 0, stream, a);
+    }
   } else if (v_channel_major) {
     launch_fp8_layout<true>(a, dqk, exact_p, g, t, stream);
   } else {

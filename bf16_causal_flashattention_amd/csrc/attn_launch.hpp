@@ -27,6 +27,7 @@ struct Fp8Args {
   TensorMap mq, mk, mv, mo;
   uint8_t* dbg_o;      // debug build only: [B*H*S][S/64] block exponents
   uint8_t* dbg_codes;  // debug build only: [B*H*S][S] probability codes
+  float* dbg_scores;   // debug build only, may be null: [B*H*S][S] raw fp32 scores (MFMA sums)
 };
 
 struct Bf16Args {

@@ -59,7 +59,10 @@ typedef enum {
  * (b, s, h, d) sits at base + b*batch + h*head + s*seq + d (the head dimension is
  * contiguous).  BSHD [B][S][H][D] is {S*H*D, D, H*D}; BHSD [B][H][S][D] is {H*S*D, S*D, D}.
  * Every stride must be >= 0 and a multiple of 16 bytes, every element offset below 2^31,
- * and 128 rows of the seq stride below 2^31 bytes; tensors must not overlap `out`. */
+ * and 128 rows of the seq stride below 2^31 bytes; tensors must not overlap `out`.
+ * The rows of `out` must not overlap one another: sorted by stride, the levels with more
+ * than one entry must each have a stride at least the span of the levels below them (so
+ * zero strides and interleaved rows are refused with ATTN_ERR_ARG). */
 typedef struct {
   int64_t batch;
   int64_t head;
@@ -197,6 +200,22 @@ int attn_round_bf16(const float* x, int64_t n, uint16_t* out, void* stream);
 int attn_fwd_causal_fp8_debug(const void* q, const void* k, const void* v, void* out, float* lse,
                               float q_descale, float k_descale, float v_descale, float softmax_scale, int B,
                               int H, int S, int d_qk, int d_v, uint8_t* dbg_o, uint8_t* dbg_codes, void* stream);
+
+/* Test hook with the arguments of attn_fwd_causal_fp8_ex (key-major V, either P mode at
+ * either head dimension) and the dumps of attn_fwd_causal_fp8_debug, plus, when dbg_scores
+ * is not NULL, the raw fp32 score s of every (b, h, query row, key) of every block the
+ * kernel processes, as the score MFMA left it and before the causal mask
+ * (dbg_scores: [B*H*S][S] floats, 16-byte aligned; entries of skipped blocks are left
+ * untouched).  These are the kernel's inputs to the decisions of paper Sec. IV-A (running
+ * maximum, lazy rescale), Sec. IV-B1 (the codes) and Sec. IV-B2 (the exponents o), so a
+ * test can re-run those decisions on them.  The outputs equal attn_fwd_causal_fp8_ex's
+ * bit for bit.  Limited to B*H*S*S <= 2^28. */
+int attn_fwd_causal_fp8_debug_ex(const void* q, const void* k, const void* v, void* out, float* lse,
+                                 float q_descale, float k_descale, float v_descale, float softmax_scale, int B,
+                                 int H, int H_kv, int S, int d_qk, int d_v, const attn_strides* q_strides,
+                                 const attn_strides* k_strides, const attn_strides* v_strides,
+                                 const attn_strides* out_strides, int p_mode, uint8_t* dbg_o, uint8_t* dbg_codes,
+                                 float* dbg_scores, void* stream);
 
 /* Host-only helpers (no device call), for schedule inspection and tests.
  * attn_default_grid: the persistent grid the attention entry points launch for a

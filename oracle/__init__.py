@@ -74,6 +74,9 @@ def lib():
         L.orc_emulate_fp8.restype = ctypes.c_int
         L.orc_emulate_fp8.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_float] * 4 + [ctypes.c_int] * 5 + \
             [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64] + [ctypes.c_void_p] * 8
+        L.orc_emulate_fp8_scores.restype = ctypes.c_int
+        L.orc_emulate_fp8_scores.argtypes = [ctypes.c_void_p] * 2 + [ctypes.c_float] * 4 + [ctypes.c_int] * 4 + \
+            [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64] + [ctypes.c_void_p] * 8
         L.orc_e4m3_rne_array.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         L.orc_bf16_rne_array.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         _lib = L
@@ -331,6 +334,52 @@ def emulate_fp8(q, k, v, *, dq: float, dk: float, dv: float, c: float, scheme: F
         _ptr(res.get("lazy_margin")))
     if rc != 0:
         raise RuntimeError(f"orc_emulate_fp8 failed: {rc}")
+    res["groups"] = groups
+    return res
+
+
+def emulate_fp8_from_scores(scores, v, *, dq: float, dk: float, dv: float, c: float, scheme: Fp8Scheme = None,
+                            groups=None, debug: bool = False):
+    """The FP8 scheme of ``emulate_fp8`` (paper Sec. IV-A, IV-B1-B3) run on given raw fp32
+    scores instead of the exact dot products of q and k.
+
+    scores: float32 [B*H*S, S], row (b*H + h)*S + i holding the raw scores of query i of
+    head (b, h) (entries j > i are not read); v: e4m3 codes [B, S, H, d_v].  For checking the
+    decisions of a kernel given the scores it computed; the parity gates use ``emulate_fp8``.
+    Returns the dict of ``emulate_fp8``."""
+    scheme = scheme or Fp8Scheme()
+    v = np.ascontiguousarray(v, dtype=np.uint8)
+    B, S, H, dvd = v.shape
+    scores = np.ascontiguousarray(scores, dtype=np.float32)
+    assert scores.shape == (B * H * S, S)
+    G = scheme.group
+    if groups is None:
+        bb, hh, rr = np.meshgrid(np.arange(B), np.arange(H), np.arange(0, S, G), indexing="ij")
+        groups = np.stack([bb.ravel(), hh.ravel(), rr.ravel()], axis=1)
+    groups = np.ascontiguousarray(np.asarray(groups, dtype=np.int64).reshape(-1, 3))
+    ng = groups.shape[0]
+    nrow = ng * G
+    nblk = (S + scheme.block - 1) // scheme.block
+    ntile = (S + scheme.n_tile - 1) // scheme.n_tile
+    res = {
+        "out": np.empty((nrow, dvd), dtype=np.float64),
+        "out_bf16": np.empty((nrow, dvd), dtype=np.uint16),
+        "lse": np.empty(nrow, dtype=np.float64),
+    }
+    if debug:
+        res["o"] = np.full((nrow, nblk), 255, dtype=np.uint8)
+        res["codes"] = np.zeros((nrow, S), dtype=np.uint8)
+        res["ymargin"] = np.full((nrow, S), np.inf, dtype=np.float32)
+        res["omargin"] = np.full((nrow, nblk), np.inf, dtype=np.float32)
+        res["lazy_margin"] = np.full((ng, ntile), np.inf, dtype=np.float32)
+    prm = scheme.c()
+    rc = lib().orc_emulate_fp8_scores(
+        _ptr(scores), _ptr(v), dq, dk, dv, c, B, H, S, dvd, ctypes.byref(prm), _ptr(groups), ng,
+        _ptr(res["out"]), _ptr(res["out_bf16"]), _ptr(res["lse"]),
+        _ptr(res.get("o")), _ptr(res.get("codes")), _ptr(res.get("ymargin")), _ptr(res.get("omargin")),
+        _ptr(res.get("lazy_margin")))
+    if rc != 0:
+        raise RuntimeError(f"orc_emulate_fp8_scores failed: {rc}")
     res["groups"] = groups
     return res
 

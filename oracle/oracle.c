@@ -22,6 +22,8 @@
  *   orc_exactp_code     exact-P code of x (round 2^(x+sigma))      paper Sec. IV-B1
  *   orc_attn_exact      exact causal softmax attention in fp64     paper Sec. II-B (definition)
  *   orc_emulate_fp8     step-by-step emulation of the FP8 scheme   paper Sec. IV-A/IV-B
+ *   orc_emulate_fp8_scores  the same scheme from given fp32 scores (checks of a kernel's
+ *                       decisions given its own scores; not a parity reference)
  */
 #include <math.h>
 #include <stdint.h>
@@ -277,11 +279,14 @@ typedef struct {
   int rounded_sum;   /* 1 l from rounded probabilities */
 } orc_fp8_params;
 
-int orc_emulate_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, float dq, float dk,
-                    float dvs, float c, int B, int H, int S, int dqk, int dv,
-                    const orc_fp8_params* prm, const int64_t* groups, int64_t n_groups,
-                    double* out, uint16_t* out_bf16, double* lse, uint8_t* o_dbg,
-                    uint8_t* code_dbg, float* ymargin, float* omargin, float* lazy_margin) {
+/* The walk itself; scores_in == NULL computes the raw scores from q and k (step 1 of the
+ * scheme), otherwise row i of head (b, h) reads them from
+ * scores_in[((b*H + h)*S + i)*S + j] (and q, k are not read).                 */
+static int emulate_walk(const float* scores_in, const uint8_t* q, const uint8_t* k, const uint8_t* v,
+                        float dq, float dk, float dvs, float c, int B, int H, int S, int dqk, int dv,
+                        const orc_fp8_params* prm, const int64_t* groups, int64_t n_groups,
+                        double* out, uint16_t* out_bf16, double* lse, uint8_t* o_dbg,
+                        uint8_t* code_dbg, float* ymargin, float* omargin, float* lazy_margin) {
   orc_init_tables();
   const int G = prm->group, NT = prm->n_tile, BK = prm->block;
   const int nblk = (S + BK - 1) / BK;
@@ -312,14 +317,20 @@ int orc_emulate_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, float 
       int nr = G;
       if (r0 + nr > S) nr = S - r0;
       int last = r0 + nr - 1; /* last row of the group */
-      /* raw scores: exact dot products of decoded codes (fits in fp64 exactly) */
+      /* raw scores: exact dot products of decoded codes (fits in fp64 exactly), or the
+       * given fp32 scores */
       for (int r = 0; r < nr; ++r) {
         int i = r0 + r;
-        for (int d = 0; d < dqk; ++d) qrow[d] = g_e4m3[q[bshd(b, i, h, d, S, H, dqk)]];
-        for (int j = 0; j <= i; ++j) {
-          double dot = 0.0;
-          for (int d = 0; d < dqk; ++d) dot += qrow[d] * g_e4m3[k[bshd(b, j, h, d, S, H, dqk)]];
-          s[(size_t)r * S + j] = dot;
+        if (scores_in) {
+          const float* srow = scores_in + (((int64_t)b * H + h) * S + i) * (int64_t)S;
+          for (int j = 0; j <= i; ++j) s[(size_t)r * S + j] = (double)srow[j];
+        } else {
+          for (int d = 0; d < dqk; ++d) qrow[d] = g_e4m3[q[bshd(b, i, h, d, S, H, dqk)]];
+          for (int j = 0; j <= i; ++j) {
+            double dot = 0.0;
+            for (int d = 0; d < dqk; ++d) dot += qrow[d] * g_e4m3[k[bshd(b, j, h, d, S, H, dqk)]];
+            s[(size_t)r * S + j] = dot;
+          }
         }
         for (int d = 0; d < dv; ++d) acc[(size_t)r * dv + d] = 0.0;
         l[r] = 0.0;
@@ -485,6 +496,30 @@ int orc_emulate_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, float 
     free(s); free(acc); free(l); free(m); free(Mn); free(qrow); free(pv);
   }
   return bad ? -bad : 0;
+}
+
+int orc_emulate_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* v, float dq, float dk,
+                    float dvs, float c, int B, int H, int S, int dqk, int dv,
+                    const orc_fp8_params* prm, const int64_t* groups, int64_t n_groups,
+                    double* out, uint16_t* out_bf16, double* lse, uint8_t* o_dbg,
+                    uint8_t* code_dbg, float* ymargin, float* omargin, float* lazy_margin) {
+  return emulate_walk(NULL, q, k, v, dq, dk, dvs, c, B, H, S, dqk, dv, prm, groups, n_groups, out,
+                      out_bf16, lse, o_dbg, code_dbg, ymargin, omargin, lazy_margin);
+}
+
+/* The same scheme from given raw fp32 scores instead of the exact dot products: steps
+ * 2-6 (running maximum and lazy rescale, Sec. IV-A; o, Sec. IV-B2; codes, Sec. IV-B1;
+ * rounded sums, Sec. IV-B3) on scores [B*H*S][S] (row (b*H + h)*S + i, only j <= i
+ * read).  For checking a kernel's decisions given the scores it computed; the parity
+ * gates use orc_emulate_fp8, whose scores are exact.                          */
+int orc_emulate_fp8_scores(const float* scores, const uint8_t* v, float dq, float dk, float dvs,
+                           float c, int B, int H, int S, int dv, const orc_fp8_params* prm,
+                           const int64_t* groups, int64_t n_groups, double* out, uint16_t* out_bf16,
+                           double* lse, uint8_t* o_dbg, uint8_t* code_dbg, float* ymargin,
+                           float* omargin, float* lazy_margin) {
+  if (!scores) return -4;
+  return emulate_walk(scores, NULL, NULL, v, dq, dk, dvs, c, B, H, S, 0, dv, prm, groups, n_groups,
+                      out, out_bf16, lse, o_dbg, code_dbg, ymargin, omargin, lazy_margin);
 }
 
 /* Bulk helpers used by tests. */

@@ -132,6 +132,18 @@ def test_ex_validation_errors(call):
     assert call(sm=0.0) == -5
 
 
+@pytest.mark.parametrize("call", [_fp8_ex, _fp8_vt, _bf16_ex])
+def test_out_rows_must_not_overlap(call):
+    # the rows of out must be disjoint: expanded (zero-stride) and interleaved views are refused
+    B, H, S = 2, 4, 256
+    assert call(B=B, H=H, so=_st(S * H * 128, 0, H * 128)) == -5     # every head writes the same row
+    assert call(B=B, H=H, so=_st(S * H * 128, 128, 0)) == -5         # every position writes the same row
+    assert call(B=B, H=H, so=_st(0, 128, H * 128)) == -5             # both batches write the same rows
+    assert call(B=B, H=H, so=_st(S * H * 128, 128, 64)) == -5        # a row overlaps the next position's
+    assert call(B=B, H=H, so=_st(S * H * 128, 128, 128)) == -5       # heads and positions interleaved
+    assert call(B=B, H=H, so=_st(S * H * 128 - 128, 128, H * 128)) == -5  # batches overlap by one row
+
+
 def test_vt_strides_checked_channel_major():
     # the channel-major V tensor is [B][H_kv][128][S]: its third stride steps between channel rows
     assert _fp8_vt(sv=_st(2 * 128 * 256, 128 * 256, 40)) == -3        # channel stride not 16-byte aligned

@@ -19,7 +19,7 @@ import bf16_causal_flashattention_amd as cfa
 import oracle
 import synth
 from gpu_util import (DEV, LSE_EMU_NATS, LSE_FP64_NATS, TOL_EMU_MAXABS, TOL_EMU_RMS, TOL_FP64_RMS_BF16,
-                      TOL_FP64_RMS_FP8, all_groups, gpu_rows, lse_rows, rms_rel)
+                      TOL_FP64_RMS_FP8, all_groups, check_fp8_on_gpu_scores, gpu_rows, lse_rows, rms_rel)
 
 pytestmark = pytest.mark.gpu
 
@@ -147,12 +147,13 @@ def _channel_major(vg, padded):
     (1, 1, 1, 256, 128, None, False),      # a single tile
 ])
 def test_fp8_vt(B, H, Hkv, S, dqk, p_mode, padded):
-    """Channel-major V: identical bit for bit to the key-major entry point, and within the
-    oracle's RMS and LSE bounds.  The element-wise max-abs gate is left out: a probability code
-    whose exact value lies within the FP8 MFMA's score-error band of a rounding boundary may
-    round either way (test_debug_codes_and_exponents checks that codes differ only there), and
-    in a row of few keys one such code moves O by more than that gate (measured: 0.026 in a
-    24-key row of the 512-key MLA case)."""
+    """Channel-major V: identical bit for bit to the key-major entry point, within the
+    oracle's RMS bounds, and element-wise (max-abs, LSE) within the gates of the emulation
+    run on the kernel's own scores.  The element-wise gate is not taken against the
+    exact-score emulation here: a probability code whose exact value lies within the FP8
+    MFMA's score-error band of a rounding boundary may round either way, and in a row of few
+    keys one such code moves O by more than that gate (0.026 in the 24-key row 23 of the
+    512-key MLA case, test_mla_short_row_regression)."""
     _case("fp8_vt", B, H, Hkv, S, dqk, p_mode, padded)
     G = H // Hkv
     q, k, v = _inputs(B, H, Hkv, S, dqk, seed=5 * S + H + dqk)
@@ -167,6 +168,23 @@ def test_fp8_vt(B, H, Hkv, S, dqk, p_mode, padded):
     (qc, _), (kc, _), (vc, _) = [oracle.quantize_e4m3(x) for x in (q, k, v)]
     exact_p = (p_mode == cfa.P_EXACT) or (p_mode is None and dqk == 192)
     _check_fp8_oracle(out, lse, qc, kc, vc, G, dq, dk, dv, c, exact_p, B, H, S, strict=False)
+    check_fp8_on_gpu_scores(qg, kg, vg, dq, dk, dv, c, p_mode, ref=(out, lse))
+
+
+def test_mla_short_row_regression():
+    """B2 H4 over 2 KV heads, S512 at the MLA shape with exact P, seed 2756: row 23 of one head
+    has 24 keys, and one of its codes sits inside the MFMA's score-error band of a rounding
+    boundary and rounds the other way than in the exact-score emulation, which moves O by
+    0.026 there.  Checked element-wise against the emulation on the kernel's own scores."""
+    B, H, Hkv, S, dqk = 2, 4, 2, 512, 192
+    _case("mla short-row regression", B, H, Hkv, S, dqk)
+    q, k, v = _inputs(B, H, Hkv, S, dqk, seed=5 * S + H + dqk)
+    gq = [cfa.quantize_e4m3(torch.from_numpy(x).to(DEV)) for x in (q, k, v)]
+    (qg, dq), (kg, dk), (vg, dv) = [(c_.view(torch.uint8), float(d_.item())) for c_, d_ in gq]
+    c = 1.0 / math.sqrt(dqk)
+    out, lse = cfa.attn_fwd_causal_fp8_ex(qg, kg, vg, dq, dk, dv, softmax_scale=c)
+    torch.cuda.synchronize()
+    check_fp8_on_gpu_scores(qg, kg, vg, dq, dk, dv, c, None, ref=(out, lse))
 
 
 @pytest.mark.parametrize("H,Hkv,dqk", [(32, 32, 128), (32, 8, 128), (16, 16, 192)])

@@ -11,11 +11,12 @@ import torch
 import bf16_causal_flashattention_amd as cfa
 import oracle
 import synth
-from gpu_util import (DEV, all_groups, check_bf16_against_oracle, check_fp8_against_oracle, fp8_entry,
-                      prep_fp8_cpu, prep_fp8_gpu, score_error_bound)
+from gpu_util import (DEV, all_groups, check_bf16_against_oracle, check_fp8_against_oracle,
+                      check_fp8_on_gpu_scores, fp8_entry, prep_fp8_gpu)
 
-# stress inputs whose logit ranges make the element-wise result depend on the FP8
-# MFMA's score precision (gated on RMS and LSE); the rest are gated element-wise too
+# stress inputs whose logit ranges make the element-wise result depend on the FP8 MFMA's
+# score precision: gated element-wise against the emulation on the kernel's own scores
+# (after checking those against the exact ones); the rest against the exact-score emulation
 WIDE = {"logit_sd_4", "logit_sd_16", "stepped_max", "full_range", "rising_logits", "alternating_rows"}
 
 pytestmark = pytest.mark.gpu
@@ -113,49 +114,25 @@ def test_bf16_stress(name):
     check_bf16_against_oracle(qkv, rows)
 
 
-# ----------------------------------------------------------------------------- bit-level debug hooks
-@pytest.mark.parametrize("dqk,S,name", [(128, 256, "gaussian"), (128, 512, "stepped_max"), (192, 512, "gaussian"),
-                                        (128, 512, "sink_flat_tail")])
-def test_debug_codes_and_exponents(dqk, S, name):
-    """Block exponents o and probability codes equal the emulation's, except where the
-    deciding fp32 quantity sits within rounding distance of its boundary."""
-    _case("debug codes", dqk, S, name)
-    B, H = 1, 1
+# ----------------------------------------------------------------------------- the kernel's own scores
+@pytest.mark.parametrize("dqk,S,name,p_mode", [
+    (128, 256, "gaussian", None), (128, 512, "stepped_max", None), (192, 512, "gaussian", None),
+    (128, 512, "sink_flat_tail", None), (128, 512, "logit_sd_16", None), (128, 512, "full_range", None),
+    (128, 512, "alternating_rows", None), (128, 512, "rising_logits", None),
+    (192, 512, "stepped_max", cfa.P_LEAN), (128, 512, "logit_sd_4", cfa.P_EXACT), (192, 512, "full_range", None)])
+def test_decisions_on_gpu_scores(dqk, S, name, p_mode):
+    """Every raw score within the MFMA bound of the exact dot product; on those scores the
+    emulation's block exponents and codes are the kernel's, bit for bit (exact P: up to
+    v_exp_f32's rounding band); O and the LSE within the gates of that emulation."""
+    _case("gpu scores", dqk, S, name, p_mode)
+    B, H = 1, 2
     gen = synth.gaussian if name == "gaussian" else synth.STRESS[name]
     q, k, v = gen(B, S, H, dqk, 128, 31)
     (qg, dq), (kg, dk), (vg, dv) = prep_fp8_gpu(q, k, v)
-    (qc, _), (kc, _), (vc, _) = prep_fp8_cpu(q, k, v)
+    qg, kg, vg = (t.view(torch.uint8) for t in (qg, kg, vg))
     c = 1 / math.sqrt(dqk)
-    _, _, go, gc = cfa.attn_fwd_causal_fp8_debug(qg, kg, vg, dq, dk, dv, softmax_scale=c)
-    torch.cuda.synchronize()
-    go, gc = go.cpu().numpy(), gc.cpu().numpy()
-    emu = oracle.emulate_fp8(qc, kc, vc, dq=dq, dk=dk, dv=dv, c=c, scheme=oracle.Fp8Scheme(exact_p=(dqk == 192)),
-                             debug=True)
-    # decisions may differ only within the score-error band of the FP8 MFMA
-    cp = c * dq * dk / math.log(2)
-    eps_t = cp * score_error_bound(qc, kc, dqk)          # per (query, key), base-2 units
-    row_eps = eps_t.max(axis=1)                           # per query row
-    grp_eps = row_eps.reshape(-1, 32).max(axis=1)
-    # a group whose lazy-rescale decision sits inside the band may follow another
-    # (equally valid) max trajectory: its codes are not unique, so it is left out
-    grp_ok = np.all(emu["lazy_margin"] > 2 * grp_eps[:, None], axis=1)
-    rows_ok = np.repeat(grp_ok, 32)[:, None]
-    assert grp_ok.mean() > 0.5
-    seen = (emu["o"] != 255) & rows_ok
-    band_o = emu["omargin"] < 2 * row_eps[:, None]
-    assert np.all((go == emu["o"])[seen] | band_o[seen])
-    mask = np.tril(np.ones((S, S), dtype=bool))
-    assert np.all(gc[~mask] == 0)  # causal mask is bit-exact
-    mask = mask & rows_ok
-    if dqk == 128:
-        band_y = emu["ymargin"] < 8 * (eps_t + row_eps[:, None])        # y = 8 (t - m + ...)
-    else:
-        band_y = emu["ymargin"] < 1.5 * (eps_t + row_eps[:, None]) + 2e-7  # relative, d p / p = ln2 dx
-    mism = (gc != emu["codes"]) & mask
-    assert not np.any(mism & ~band_y), int(np.sum(mism & ~band_y))
-    assert np.all(np.abs(gc[mism].astype(int) - emu["codes"][mism].astype(int)) <= 1)
-    print("code mismatches inside the score-error band:", int(mism.sum()), "of", int(mask.sum()),
-          "; o mismatches:", int(((go != emu["o"]) & seen).sum()))
+    ref = cfa.attn_fwd_causal_fp8_ex(qg, kg, vg, dq, dk, dv, softmax_scale=c, p_mode=p_mode)
+    check_fp8_on_gpu_scores(qg, kg, vg, dq, dk, dv, c, p_mode, ref=ref)
 
 
 # ----------------------------------------------------------------------------- closed forms on the GPU
