@@ -75,6 +75,7 @@ def lib():
         L.attn_key_mean_workspace.argtypes = [I, I, I, I]
         L.attn_key_mean_workspace.restype = I64
         L.attn_key_mean.argtypes = [P, I, I, I, I, P, P, P]
+        L.attn_key_mean_noalloc.argtypes = [P, I, I, I, I, P, P]
         L.attn_rotate_quantize_e4m3.argtypes = [P, P, P, I, I, I, I, P, P, P, P]
         L.attn_quantize_e4m3_static.argtypes = [P, I64, F, P, P]
         L.attn_rotate_quantize_e4m3_static.argtypes = [P, P, P, I, I, I, I, F, P, P]
@@ -87,6 +88,7 @@ def lib():
                      "attn_fwd_causal_fp8_debug_ex",
                      "attn_fwd_causal_bf16", "attn_fwd_causal_fp8_ex", "attn_fwd_causal_fp8_vt", "attn_fwd_causal_bf16_ex",
                      "attn_quantize_e4m3", "attn_round_bf16", "attn_default_grid", "attn_key_mean",
+                     "attn_key_mean_noalloc",
                      "attn_rotate_quantize_e4m3", "attn_quantize_e4m3_static", "attn_rotate_quantize_e4m3_static"):
             getattr(L, name).restype = I
         _lib = L
@@ -337,6 +339,18 @@ def key_mean(k):
     ws = torch.empty(max((int(n_ws) + 7) // 8, 1), dtype=torch.float64, device=k.device)
     _check("attn_key_mean", L.attn_key_mean(_ptr(k), B, S, H, D, _ptr(mean), _ptr(ws), _stream(k)))
     return mean
+
+
+def key_mean_noalloc(k, out):
+    """attn_key_mean_noalloc: the mean key of each head of k [B, S, H, D] written into out, a
+    contiguous float32 [B, H, D] GPU tensor, with no device allocation (the partial sums use the
+    library's static scratch array; calls on one GPU must not overlap).  Returns out."""
+    B, S, H, D = _bshd_f32(k, "k")
+    if out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != (B, H, D):
+        raise ValueError("out must be a contiguous float32 [B, H, D] tensor")
+    _same_device(k, out)
+    _check("attn_key_mean_noalloc", lib().attn_key_mean_noalloc(_ptr(k), B, S, H, D, _ptr(out), _stream(k)))
+    return out
 
 
 def _rot_checks(x, signs, mean):

@@ -367,6 +367,19 @@ int attn_key_mean(const float* k, int B, int S, int H, int D, float* mean, void*
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
+int attn_key_mean_noalloc(const float* k, int B, int S, int H, int D, float* mean, void* stream) {
+  if (B < 0 || S < 0 || H < 0 || (D != 128 && D != 192)) return ATTN_ERR_SHAPE;
+  if (B == 0 || H == 0) return ATTN_OK;
+  if (S == 0) return ATTN_ERR_SHAPE;
+  if (!k || !mean) return ATTN_ERR_NULL;
+  if (!aligned(k, 4) || !aligned(mean, 4)) return ATTN_ERR_ALIGN;
+  if ((int64_t)B * S * H * D >= (INT64_C(1) << 31) || (int64_t)B * H >= 65536) return ATTN_ERR_RANGE;
+  if (cfa::key_mean_workspace_bytes(B, S, H, D) > cfa::kKeyMeanScratchBytes) return ATTN_ERR_SCRATCH;
+  const hipError_t e = cfa::launch_key_mean_noalloc(k, B, S, H, D, mean, (hipStream_t)stream);
+  if (e == hipErrorNoDevice || e == hipErrorInvalidDevice) return ATTN_ERR_DEVICE;
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
 int attn_rotate_quantize_e4m3(const float* x, const float* mean, const float* signs, int B, int S, int H, int D,
                               uint8_t* codes, float* descale, uint32_t* workspace, void* stream) {
   const int rc = check_rotate(x, mean, signs, B, S, H, D, codes);
@@ -455,6 +468,8 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_ARG: return "invalid argument (scales must be finite and positive)";
     case ATTN_ERR_LAUNCH: return "kernel launch failed";
     case ATTN_ERR_DEVICE: return "no usable HIP device";
+    case ATTN_ERR_SCRATCH:
+      return "problem needs more scratch memory than the allocation-free entry point holds";
     default: return "unknown status";
   }
 }

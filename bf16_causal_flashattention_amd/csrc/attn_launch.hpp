@@ -49,6 +49,11 @@ hipError_t launch_quantize_e4m3(const float* x, int64_t n, uint8_t* codes, float
                                 hipStream_t stream);
 hipError_t launch_round_bf16(const float* x, int64_t n, uint16_t* out, hipStream_t stream);
 int64_t key_mean_workspace_bytes(int B, int S, int H, int D);
+// size of the file-scope partial-sum array of the allocation-free key mean
+constexpr int64_t kKeyMeanScratchBytes = INT64_C(4) << 20;
+// the key mean with its partial sums in that array (per device; calls on one GPU must not
+// overlap); B * H * ceil(S / 1024) * D * 8 bytes must not exceed kKeyMeanScratchBytes
+hipError_t launch_key_mean_noalloc(const float* k, int B, int S, int H, int D, float* mean, hipStream_t stream);
 hipError_t launch_key_mean(const float* k, int B, int S, int H, int D, float* mean, void* ws, hipStream_t stream);
 // static_scale / is_static: one pass with the given power-of-two scale (saturating at 448)
 // instead of the two-pass maximum-derived scale (descale and ws unused then).

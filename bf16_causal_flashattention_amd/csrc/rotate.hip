@@ -26,6 +26,8 @@
 // stays in registers; (x - m) s is then one exact fma(x, s, -m s).  In the two-pass form
 // both passes run the same instructions, so both see identical values and the rotated
 // tensor is never stored.
+#include <atomic>
+
 #include "attn_common.hpp"
 #include "attn_launch.hpp"
 
@@ -351,6 +353,35 @@ hipError_t launch_key_mean(const float* k, int B, int S, int H, int D, float* me
   hipLaunchKernelGGL(key_mean_final_kernel, dim3(B * H), dim3(D), 0, stream, (const double*)part, S, D, nchunk,
                      mean);
   return hipGetLastError();
+}
+
+// Allocation-free key mean: the fp64 partial sums live in this file-scope device array
+// instead of a caller workspace.  Every GPU that runs it holds its own copy until the process
+// ends, at its own address; host code reaches it only through the address that
+// hipGetSymbolAddress returns on that device (the array's name is not a device address in
+// host code).  Every call on one GPU reuses that GPU's copy: the partial kernel overwrites
+// each partial sum it later reads, so nothing needs clearing, and calls that overlap on one
+// GPU race.
+static __device__ __align__(256) double scratch[kKeyMeanScratchBytes / sizeof(double)];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];  // per device; null until looked up
+}  // namespace
+
+hipError_t launch_key_mean_noalloc(const float* k, int B, int S, int H, int D, float* mean, hipStream_t stream) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {  // first call on this device, which is current: look its copy up once
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return launch_key_mean(k, B, S, H, D, mean, p, stream);
 }
 
 hipError_t launch_rotate_quantize(const float* x, const float* mean, const float* signs, int B, int S, int H,

@@ -52,7 +52,8 @@ typedef enum {
   ATTN_ERR_RANGE = -4,  /* a tensor has 2^31 elements or more */
   ATTN_ERR_ARG = -5,    /* a scale is not finite and positive, or a bad size argument */
   ATTN_ERR_LAUNCH = -6, /* the kernel launch failed (hipGetLastError) */
-  ATTN_ERR_DEVICE = -7  /* no usable device / device query failed */
+  ATTN_ERR_DEVICE = -7, /* no usable device / device query failed */
+  ATTN_ERR_SCRATCH = -8 /* the allocation-free entry point's scratch array is too small */
 } attn_status;
 
 /* Element strides of one attention tensor for the *_ex entry points: element
@@ -158,6 +159,17 @@ int attn_quantize_e4m3(const float* x, int64_t n, uint8_t* codes, float* descale
  * B = 0 or H = 0 is a no-op. */
 int64_t attn_key_mean_workspace(int B, int S, int H, int D);
 int attn_key_mean(const float* k, int B, int S, int H, int D, float* mean, void* workspace, void* stream);
+
+/* attn_key_mean for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels and
+ * results, with the fp64 partial sums in a static 4 MiB device array of the library instead
+ * of a caller workspace.  The call allocates nothing.  Each GPU it runs on holds its own
+ * copy of the array until the process ends.  Needs B*H*ceil(S/1024)*D*8 <= 4 MiB
+ * (B*H*ceil(S/1024)*D <= 524288, e.g. B = 1, H = 32, S = 131072, D = 128), else
+ * ATTN_ERR_SCRATCH and nothing is launched.  Every call on one GPU uses that GPU's array:
+ * calls that overlap on one GPU (other streams or host threads) race and must be
+ * serialised by the caller.  Other arguments and errors as for attn_key_mean. */
+int attn_key_mean_noalloc(const float* k, int B, int S, int H, int D, float* mean, void* stream);
 
 /* Quantisation pre-pass with rotation (paper Sec. V-E, "Rotation and K smoothing", and
  * Table XIII): y = (x - mean[b][h]) R with R = diag(signs) (C_m kron H_{D/m}), H the

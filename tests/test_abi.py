@@ -194,6 +194,18 @@ def test_prep_validation():
     assert L.attn_round_bf16(FAKE, 0, None, None) == 0
 
 
+def test_key_mean_noalloc_validation():
+    L = cfa.lib()
+    assert L.attn_key_mean_noalloc(FAKE, 1, 1 << 17, 64, 128, FAKE, None) == -8   # 8 MiB of partials > 4 MiB
+    assert L.attn_key_mean_noalloc(FAKE, 2, 1 << 16, 33, 128, FAKE, None) == -8   # 4.1 MiB
+    assert L.attn_key_mean_noalloc(FAKE, 1, 256, 1, 96, FAKE, None) == -2
+    assert L.attn_key_mean_noalloc(FAKE, 1, 0, 1, 128, FAKE, None) == -2
+    assert L.attn_key_mean_noalloc(None, 0, 256, 1, 128, None, None) == 0
+    assert L.attn_key_mean_noalloc(None, 1, 256, 1, 128, FAKE, None) == -1
+    assert L.attn_key_mean_noalloc(FAKE, 1, 256, 1, 128, ctypes.c_void_p((1 << 20) + 2), None) == -3
+    assert cfa.lib().attn_status_string(-8).decode().startswith("problem needs more scratch")
+
+
 def test_rotation_prepass_validation():
     L = cfa.lib()
     odd = ctypes.c_void_p((1 << 20) + 2)  # not 4-byte aligned
