@@ -11,23 +11,28 @@
 //   Sec. IV-B3         row sum of the rounded probabilities on the matrix unit;
 //   Sec. IV-C, Fig. 6  two-wave ping-pong: the two waves of a SIMD alternate between an
 //                      MFMA phase and a softmax phase, with a workgroup barrier per phase.
-//                      Here the softmax phase also takes the block maximum and the
-//                      rescale decision, so the MFMA wave's stream is MFMAs and operand
-//                      reads only.
+//                      At d_qk = 128 with key-major V the matrix phase is one block of
+//                      hand-ordered instructions and, as the paper's MFMA wave does, takes
+//                      the block maxima of the next block between its PV MFMAs; elsewhere
+//                      the softmax phase takes them.
 //
 // Schedule per 256-row tile with nb 128-key blocks.  Group g = wave / 4 (one wave of
 // each group per SIMD).  Group 1 runs one phase behind group 0:
 //   group 0:  M_pro S_pro M_0 S_0 M_1 S_1 ... M_{nb-1} S_{nb-1} idle
 //   group 1:  idle  M_pro S_pro M_0 S_0 ... M_{nb-1} S_{nb-1}
-// M_i (matrix phase): row sums of P(i); S(i+1) = K(i+1) Q^T; O += V(i)^T P(i); l update.
-// S_i (softmax phase): maximum of S(i+1), lazy decision (and the rare rescale of O and
-//      l), o(i+1), P(i+1).  The matrix wave issues only MFMAs and their LDS operand reads.
+// M_i (matrix phase): row sums of P(i); S(i+1) = K(i+1) Q^T; O += V(i)^T P(i); l update;
+//      at d_qk = 128 with key-major V also the block maxima of S(i+1) (blocks below the
+//      diagonal; the softmax phase redoes them with the causal mask on the diagonal).
+// S_i (softmax phase): block maxima of S(i+1) where the matrix phase did not take them,
+//      lazy decision (and the rare rescale of O and l), o(i+1), P(i+1).
 // Staging by DMA (global_load_lds, no registers): at the end of M_i, after its last
 // operand read, group 0 copies K(i+2) into the slot of K(i) (two K slots) and group 1
 // copies V(i+2) into the slot of V(i-1) (three V slots); each wave waits for its copies at
 // the end of S_i.  Every target slot was last read in an earlier phase, every copy
 // completes at least one phase before its first read, and the softmax phase reads no
-// LDS, so nothing waits on a copy early.
+// LDS, so nothing waits on a copy early.  In the hand-ordered matrix phase every step
+// copies: in a tile's last two steps, which have no block i+2, the wave copies the tile's
+// last block again into the slot the schedule frees.
 // Epilogue: after the tile's last barrier no wave reads K or V, so each wave writes its
 // 32 rows of bf16 O into a staging area of its own at the start of LDS and stores them
 // as whole 256-byte rows; a barrier keeps the next tile's copies out until every wave
@@ -113,6 +118,10 @@ __device__ __forceinline__ float max2(float a, float b) {
   return r;
 }
 
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_void_t*)p;
+}
+
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -179,6 +188,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
     }
   }
   const int st_lds = 16 * 64 * wq + (stage_k ? 0 : L::kVBase);
+  // whether this wave has a fifth 64-cell copy round (K: waves 0, 1 of group 0; V: wave 0 of
+  // group 1), for the hand-ordered matrix phase
+  const uint32_t round5 = ((stage_k ? 3u : 1u) >> wq) & 1u;
 
   // row-sum selector (Sec. IV-B3): lane L of the 16x16x128 A operand is all ones
   // iff (L/16)%2 == ((L%16)/4)%2, so every lane receives the sum of its own query.
@@ -304,9 +316,223 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
         }
       };
+      // The matrix phase at d_qk = 128 with key-major V, as one block of hand-ordered
+      // instructions that every step of every wave runs: the row sums of P(i), S^T(i+1) = K Q^T
+      // (8 MFMAs), O^T += V^T(i) P^T(i) (8 MFMAs), and between the PV MFMAs the maxima of the two
+      // 64-key blocks of S(i+1) (the paper's MFMA wave computes them too, Sec. IV-C; the softmax
+      // phase then only takes the lazy decision, o and the codes), then the wave's copies of
+      // block i+2.  The first K operand read goes out before the row-sum MFMAs, each later
+      // operand read two MFMAs ahead of its MFMA, the first two V^T operands during the last two
+      // QK^T MFMAs; every read is waited for inside the block.  K and V^T operands pass through
+      // two fixed 8-register groups (v240-v255; the second carries the 0/1 row-sum selector
+      // first), and the scores sit in v176-v239 so that the maxima can name them.  Copies go
+      // through a scalar base and the per-lane 32-bit offsets, with M0 saved and restored.
+      // Wait states: five before the first copy may read the scalar base (a compiler reload of
+      // it may come just before the block), two after the selector moves and after the
+      // permlane operands are written, one after each M0 write; the instructions after the last
+      // PV MFMA cover the 20 that a VALU read of its results needs.
+      float bmx[2] = {0.f, 0.f};  // block maxima of the next block from the hand-ordered matrix phase
+      float bm[2];
+      auto mphase_asm = [&](int i) -> v2f {
+        const uint32_t kb = lds_addr(smem) + ((i + 1) & 1) * L::kKSlot + k_rd;
+        const uint32_t vb = lds_addr(smem) + (i % 3) * L::kVSlot + v_tr;
+        const int sc0 = 127 - o_cur[0], sc1 = 127 - o_cur[1], one = 127;
+        // in a tile's last two steps there is no block i+2: the wave then copies the tile's last
+        // block again into the slot the schedule frees (no wave reads it before it is written
+        // again), so every step runs the same instructions; the copies are waited for as usual
+        const int blk = i + 2 < nb ? i + 2 : nb - 1;
+        const uint8_t* src = st_head + blk * st_bstep;
+        const uint32_t mb = __builtin_amdgcn_readfirstlane(
+            lds_addr(smem) + st_lds + (stage_k ? ((i + 2) & 1) * L::kKSlot : ((i + 2) % 3) * L::kVSlot));
+        const uint64_t gs = (uint64_t)(uintptr_t)src;  // wave-uniform: scalar base of the copies
+        int m0s;
+        float xt0, xt1;
+        v4f b0, b1;
+        v8i g0, g1;  // the operand groups, clobbered
+        asm volatile(
+            // wait states before the first copy's scalar base (a compiler reload of it may precede)
+            "s_nop 4\n\t"
+            "s_mov_b32 %[m0s], m0\n\t"
+            "s_waitcnt lgkmcnt(0)\n\t"
+            // row sums of P(i): the 0/1 selector in group 1, the first K operand read in group 0
+            "v_mov_b32 v248, %[selw]\n\t"
+            "v_mov_b32 v249, %[selw]\n\t"
+            "v_mov_b32 v250, %[selw]\n\t"
+            "v_mov_b32 v251, %[selw]\n\t"
+            "v_mov_b32 v252, %[selw]\n\t"
+            "v_mov_b32 v253, %[selw]\n\t"
+            "v_mov_b32 v254, %[selw]\n\t"
+            "v_mov_b32 v255, %[selw]\n\t"
+            "ds_read_b128 v[240:243], %[kb]\n\t"
+            "ds_read_b128 v[244:247], %[kb] offset:16\n\t"
+            "s_nop 1\n\t"
+            "v_mfma_scale_f32_16x16x128_f8f6f4 %[b0], v[248:255], %[p0], 0, %[one], %[one] op_sel_hi:[0,0,0]\n\t"
+            "v_mfma_scale_f32_16x16x128_f8f6f4 %[b1], v[248:255], %[p1], 0, %[one], %[one] op_sel_hi:[0,0,0]\n\t"
+            // S^T(i+1) = K Q^T: sub-tile u, 64-wide chunk c, chunk-outer; each operand read two MFMAs ahead
+            "ds_read_b128 v[248:251], %[kb] offset:4608\n\t"
+            "ds_read_b128 v[252:255], %[kb] offset:4624\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 v[176:191], v[240:247], %[q0], 0, %[one], %[one] op_sel_hi:[0,0,0]\n\t"
+            "ds_read_b128 v[240:243], %[kb] offset:9216\n\t"
+            "ds_read_b128 v[244:247], %[kb] offset:9232\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 v[192:207], v[248:255], %[q0], 0, %[one], %[one] op_sel_hi:[0,0,0]\n\t"
+            "ds_read_b128 v[248:251], %[kb] offset:13824\n\t"
+            "ds_read_b128 v[252:255], %[kb] offset:13840\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 v[208:223], v[240:247], %[q0], 0, %[one], %[one] op_sel_hi:[0,0,0]\n\t"
+            "ds_read_b128 v[240:243], %[kb] offset:64\n\t"
+            "ds_read_b128 v[244:247], %[kb] offset:80\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 v[224:239], v[248:255], %[q0], 0, %[one], %[one] op_sel_hi:[0,0,0]\n\t"
+            "ds_read_b128 v[248:251], %[kb] offset:4672\n\t"
+            "ds_read_b128 v[252:255], %[kb] offset:4688\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 v[176:191], v[240:247], %[q1], v[176:191], %[one], %[one] op_sel_hi:[0,0,0]\n\t"
+            "ds_read_b128 v[240:243], %[kb] offset:9280\n\t"
+            "ds_read_b128 v[244:247], %[kb] offset:9296\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 v[192:207], v[248:255], %[q1], v[192:207], %[one], %[one] op_sel_hi:[0,0,0]\n\t"
+            "ds_read_b128 v[248:251], %[kb] offset:13888\n\t"
+            "ds_read_b128 v[252:255], %[kb] offset:13904\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 v[208:223], v[240:247], %[q1], v[208:223], %[one], %[one] op_sel_hi:[0,0,0]\n\t"
+            // the first two V^T operands of PV(i), four transpose reads each
+            "ds_read_b64_tr_b8 v[240:241], %[vb]\n\t"
+            "ds_read_b64_tr_b8 v[242:243], %[vb] offset:256\n\t"
+            "ds_read_b64_tr_b8 v[244:245], %[vb] offset:4224\n\t"
+            "ds_read_b64_tr_b8 v[246:247], %[vb] offset:4480\n\t"
+            "s_waitcnt lgkmcnt(4)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 v[224:239], v[248:255], %[q1], v[224:239], %[one], %[one] op_sel_hi:[0,0,0]\n\t"
+            "ds_read_b64_tr_b8 v[248:249], %[vb] offset:32\n\t"
+            "ds_read_b64_tr_b8 v[250:251], %[vb] offset:288\n\t"
+            "ds_read_b64_tr_b8 v[252:253], %[vb] offset:4256\n\t"
+            "ds_read_b64_tr_b8 v[254:255], %[vb] offset:4512\n\t"
+            "s_waitcnt lgkmcnt(4)\n\t"
+            // O^T += V^T(i) P^T(i) with the 2^-o scale of each 64-key block; between these MFMAs the maxima
+            // of the two 64-key blocks of S(i+1), each a v_max3 chain over a lane's 32 scores of the block
+            // (the scores were written five or more MFMAs earlier)
+            "v_mfma_scale_f32_32x32x64_f8f6f4 %[o0], v[240:247], %[p0], %[o0], %[one], %[c0] op_sel_hi:[0,0,0]\n\t"
+            "ds_read_b64_tr_b8 v[240:241], %[vb] offset:64\n\t"
+            "ds_read_b64_tr_b8 v[242:243], %[vb] offset:320\n\t"
+            "ds_read_b64_tr_b8 v[244:245], %[vb] offset:4288\n\t"
+            "ds_read_b64_tr_b8 v[246:247], %[vb] offset:4544\n\t"
+            "s_waitcnt lgkmcnt(4)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 %[o1], v[248:255], %[p0], %[o1], %[one], %[c0] op_sel_hi:[0,0,0]\n\t"
+            "ds_read_b64_tr_b8 v[248:249], %[vb] offset:96\n\t"
+            "ds_read_b64_tr_b8 v[250:251], %[vb] offset:352\n\t"
+            "ds_read_b64_tr_b8 v[252:253], %[vb] offset:4320\n\t"
+            "ds_read_b64_tr_b8 v[254:255], %[vb] offset:4576\n\t"
+            "v_max3_f32 %[t0], v176, v177, v178\n\t"
+            "v_max3_f32 %[t0], %[t0], v179, v180\n\t"
+            "v_max3_f32 %[t0], %[t0], v181, v182\n\t"
+            "v_max3_f32 %[t0], %[t0], v183, v184\n\t"
+            "v_max3_f32 %[t0], %[t0], v185, v186\n\t"
+            "v_max3_f32 %[t0], %[t0], v187, v188\n\t"
+            "s_waitcnt lgkmcnt(4)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 %[o2], v[240:247], %[p0], %[o2], %[one], %[c0] op_sel_hi:[0,0,0]\n\t"
+            "ds_read_b64_tr_b8 v[240:241], %[vb] offset:8448\n\t"
+            "ds_read_b64_tr_b8 v[242:243], %[vb] offset:8704\n\t"
+            "ds_read_b64_tr_b8 v[244:245], %[vb] offset:12672\n\t"
+            "ds_read_b64_tr_b8 v[246:247], %[vb] offset:12928\n\t"
+            "v_max3_f32 %[t0], %[t0], v189, v190\n\t"
+            "v_max3_f32 %[t0], %[t0], v191, v192\n\t"
+            "v_max3_f32 %[t0], %[t0], v193, v194\n\t"
+            "v_max3_f32 %[t0], %[t0], v195, v196\n\t"
+            "v_max3_f32 %[t0], %[t0], v197, v198\n\t"
+            "s_waitcnt lgkmcnt(4)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 %[o3], v[248:255], %[p0], %[o3], %[one], %[c0] op_sel_hi:[0,0,0]\n\t"
+            "ds_read_b64_tr_b8 v[248:249], %[vb] offset:8480\n\t"
+            "ds_read_b64_tr_b8 v[250:251], %[vb] offset:8736\n\t"
+            "ds_read_b64_tr_b8 v[252:253], %[vb] offset:12704\n\t"
+            "ds_read_b64_tr_b8 v[254:255], %[vb] offset:12960\n\t"
+            "v_max3_f32 %[t0], %[t0], v199, v200\n\t"
+            "v_max3_f32 %[t0], %[t0], v201, v202\n\t"
+            "v_max3_f32 %[t0], %[t0], v203, v204\n\t"
+            "v_max3_f32 %[t0], %[t0], v205, v206\n\t"
+            "v_max_f32 %[t0], %[t0], v207\n\t"
+            "s_waitcnt lgkmcnt(4)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 %[o0], v[240:247], %[p1], %[o0], %[one], %[c1] op_sel_hi:[0,0,0]\n\t"
+            "ds_read_b64_tr_b8 v[240:241], %[vb] offset:8512\n\t"
+            "ds_read_b64_tr_b8 v[242:243], %[vb] offset:8768\n\t"
+            "ds_read_b64_tr_b8 v[244:245], %[vb] offset:12736\n\t"
+            "ds_read_b64_tr_b8 v[246:247], %[vb] offset:12992\n\t"
+            "v_max3_f32 %[t1], v208, v209, v210\n\t"
+            "v_max3_f32 %[t1], %[t1], v211, v212\n\t"
+            "v_max3_f32 %[t1], %[t1], v213, v214\n\t"
+            "v_max3_f32 %[t1], %[t1], v215, v216\n\t"
+            "v_max3_f32 %[t1], %[t1], v217, v218\n\t"
+            "v_max3_f32 %[t1], %[t1], v219, v220\n\t"
+            "s_waitcnt lgkmcnt(4)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 %[o1], v[248:255], %[p1], %[o1], %[one], %[c1] op_sel_hi:[0,0,0]\n\t"
+            "ds_read_b64_tr_b8 v[248:249], %[vb] offset:8544\n\t"
+            "ds_read_b64_tr_b8 v[250:251], %[vb] offset:8800\n\t"
+            "ds_read_b64_tr_b8 v[252:253], %[vb] offset:12768\n\t"
+            "ds_read_b64_tr_b8 v[254:255], %[vb] offset:13024\n\t"
+            "v_max3_f32 %[t1], %[t1], v221, v222\n\t"
+            "v_max3_f32 %[t1], %[t1], v223, v224\n\t"
+            "v_max3_f32 %[t1], %[t1], v225, v226\n\t"
+            "v_max3_f32 %[t1], %[t1], v227, v228\n\t"
+            "v_max3_f32 %[t1], %[t1], v229, v230\n\t"
+            "s_waitcnt lgkmcnt(4)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 %[o2], v[240:247], %[p1], %[o2], %[one], %[c1] op_sel_hi:[0,0,0]\n\t"
+            "v_max3_f32 %[t1], %[t1], v231, v232\n\t"
+            "v_max3_f32 %[t1], %[t1], v233, v234\n\t"
+            "v_max3_f32 %[t1], %[t1], v235, v236\n\t"
+            "v_max3_f32 %[t1], %[t1], v237, v238\n\t"
+            "v_max_f32 %[t1], %[t1], v239\n\t"
+            "s_waitcnt lgkmcnt(0)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 %[o3], v[248:255], %[p1], %[o3], %[one], %[c1] op_sel_hi:[0,0,0]\n\t"
+            // the two lanes of a query hold keys 16 hh + r: combine them, then scale to base-2 units
+            "v_mov_b32 %[x0], %[t0]\n\t"
+            "v_mov_b32 %[x1], %[t1]\n\t"
+            "s_nop 1\n\t"
+            "v_permlane32_swap_b32 %[t0], %[x0]\n\t"
+            "v_permlane32_swap_b32 %[t1], %[x1]\n\t"
+            "s_nop 1\n\t"
+            "v_max_f32 %[t0], %[t0], %[x0]\n\t"
+            "v_mul_f32 %[t0], %[cp], %[t0]\n\t"
+            "v_max_f32 %[t1], %[t1], %[x1]\n\t"
+            "v_mul_f32 %[t1], %[cp], %[t1]\n\t"
+            // the wave's copies of block i+2: four 64-cell rounds, and a fifth for the waves that have one;
+            // these instructions also cover the wait states a VALU read of the last PV results needs
+            "s_mov_b32 m0, %[mb]\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %[a0], %[gs]\n\t"
+            "s_add_u32 m0, %[mb], 4096\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %[a1], %[gs]\n\t"
+            "s_add_u32 m0, %[mb], 8192\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %[a2], %[gs]\n\t"
+            "s_add_u32 m0, %[mb], 12288\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %[a3], %[gs]\n\t"
+            "s_cmp_eq_u32 %[five], 0\n\t"
+            "s_cbranch_scc1 1f\n\t"
+            "s_add_u32 m0, %[mb], 16384\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %[a4], %[gs]\n\t"
+            "1:\n\t"
+            "s_mov_b32 m0, %[m0s]\n\t"
+            : "=&{v[176:191]}"(sacc[0]), "=&{v[192:207]}"(sacc[1]), "=&{v[208:223]}"(sacc[2]),
+              "=&{v[224:239]}"(sacc[3]), [t0] "=&v"(bmx[0]), [t1] "=&v"(bmx[1]), [x0] "=&v"(xt0), [x1] "=&v"(xt1),
+              [o0] "+v"(oacc[0]), [o1] "+v"(oacc[1]), [o2] "+v"(oacc[2]), [o3] "+v"(oacc[3]),
+              [b0] "=&v"(b0), [b1] "=&v"(b1), "=&{v[240:247]}"(g0), "=&{v[248:255]}"(g1), [m0s] "=&s"(m0s)
+            : [kb] "v"(kb), [vb] "v"(vb), [q0] "v"(qop[0]), [q1] "v"(qop[1]), [p0] "v"(pb[0]), [p1] "v"(pb[1]),
+              [selw] "v"(selw), [one] "v"(one), [c0] "v"(sc0), [c1] "v"(sc1), [mb] "s"(mb), [gs] "s"(gs),
+              [a0] "v"(st_goff[0]), [a1] "v"(st_goff[1]), [a2] "v"(st_goff[2]), [a3] "v"(st_goff[3]),
+              [a4] "v"(st_goff[NR > 4 ? 4 : 0]), [five] "s"(round5), [cp] "s"(cp)
+            : "memory", "scc");
+        (void)g0;
+        (void)g1;
+        (void)xt0;
+        (void)xt1;
+        return (v2f){b0[0], b1[0]};
+      };
       // causal mask, block maxima (v_max3 tree), running max with the lazy decision (the
       // rare rescale of O and l happens here, in the softmax phase), exponents o for blk
-      auto max_step = [&](int blk, bool first) {
+      auto dump_scores = [&](int blk) {
         const int key0 = blk * kBlockKeys;
         if constexpr (DEBUG) {  // raw scores as the MFMA left them, before the mask
           if (a.dbg_scores != nullptr) {
@@ -318,6 +544,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
                 *(v4f*)(srow + 32 * u + r) = (v4f){sacc[u][r], sacc[u][r + 1], sacc[u][r + 2], sacc[u][r + 3]};
           }
         }
+      };
+      auto block_max = [&](int blk) {
+        const int key0 = blk * kBlockKeys;
         if (key0 + kBlockKeys - 1 > row0) {  // diagonal block: key key0+32u+16hh+r
 #pragma unroll
           for (int u = 0; u < 4; ++u)
@@ -325,7 +554,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
             for (int r = 0; r < 16; ++r)
               if (key0 + 32 * u + 16 * hh + r > qrow) sacc[u][r] = -INFINITY;
         }
-        float bm[2];
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
           float x[11];
@@ -343,6 +571,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
           const float ya = __uint_as_float(sw[0]), yb = __uint_as_float(sw[1]);
           bm[n] = max2(ya, yb) * cp;
         }
+      };
+      auto decide = [&](bool first) {
         if (first) {
           m = fmaxf(bm[0], bm[1]);
         } else {
@@ -423,7 +653,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
       lds_barrier();
       // S_pro
       if (live(0)) {
-        max_step(0, true);
+        dump_scores(0);
+        block_max(0);
+        decide(true);
         codes(0);
       }
       lds_barrier();
@@ -432,24 +664,48 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
         // -------------------------------------------------------------- M_i
         __builtin_amdgcn_s_setprio(1);
         const bool live_i = live(i), live_n = (i + 1 < nb) && live(i + 1);
-        v2f bsum = {0.f, 0.f};
-        if (live_i) bsum = rowsum();
-        if (live_n) qk(i + 1);
-        if (live_i) {
-          pv(i);
+        if constexpr (DQK == 128 && !VT) {
+          // every wave runs the whole stream: a block the causal mask hides from all rows of the
+          // wave has zero codes (set in the softmax phase), so its PV and row sums add 0, and the
+          // scores of a dead or missing next block (its K slot holds an earlier block, in
+          // bounds) are never read
+          v2f bsum;
+          bsum = mphase_asm(i);
           l = fmaf(bsum[1], __int_as_float((127 - o_cur[1]) << 23), fmaf(bsum[0], __int_as_float((127 - o_cur[0]) << 23), l));
+        } else {
+          v2f bsum = {0.f, 0.f};
+          if (live_i) bsum = rowsum();
+          if (live_n) qk(i + 1);
+          if (live_i) {
+            pv(i);
+            l = fmaf(bsum[1], __int_as_float((127 - o_cur[1]) << 23), fmaf(bsum[0], __int_as_float((127 - o_cur[0]) << 23), l));
+          }
+          // after this phase's last operand read: K(i+2) by group 0 into the slot of K(i),
+          // V(i+2) by group 1 into the slot of V(i-1); waited for at the end of S_i
+          if (i + 2 < nb) stage(i + 2);
         }
-        // after this phase's last operand read: K(i+2) by group 0 into the slot of K(i),
-        // V(i+2) by group 1 into the slot of V(i-1); waited for at the end of S_i
-        if (i + 2 < nb) stage(i + 2);
         lds_barrier();
         // -------------------------------------------------------------- S_i
         __builtin_amdgcn_s_setprio(0);
         if (live_n) {
-          max_step(i + 1, false);
+          dump_scores(i + 1);
+          if (DQK == 128 && !VT && (i + 1) * kBlockKeys + kBlockKeys - 1 <= row0) {
+            // below the diagonal for every row of the wave: the matrix phase took the maxima
+            bm[0] = bmx[0];
+            bm[1] = bmx[1];
+          } else {
+            block_max(i + 1);
+          }
+          decide(false);
           codes(i + 1);
+        } else if constexpr (DQK == 128 && !VT) {
+#pragma unroll
+          for (int n = 0; n < 2; ++n) {
+            pb[n] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+            o_cur[n] = 0;
+          }
         }
-        if (i + 2 < nb) wait_dma();
+        if ((DQK == 128 && !VT) || i + 2 < nb) wait_dma();
         lds_barrier();
       }
       if (grp == 0) lds_barrier();

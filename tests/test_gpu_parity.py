@@ -166,6 +166,9 @@ def test_one_hot_returns_value_row(dqk):
 # ----------------------------------------------------------------------------- determinism and coverage
 @pytest.mark.parametrize("kind", ["fp8", "mla", "bf16"])
 def test_bitwise_reproducible_with_interferer(kind):
+    """200 launches, bit for bit equal to the first, with an interferer before each: a BF16
+    GEMM and a BF16 attention call in turn (paper Table XII), the latter on a second stream
+    so that it overlaps the checked launch."""
     _case("determinism", kind)
     B, H, S = 1, 8, 2048
     dqk = 192 if kind == "mla" else 128
@@ -178,14 +181,22 @@ def test_bitwise_reproducible_with_interferer(kind):
         run = lambda: fp8_entry(dqk)(qg, kg, vg, dq, dk, dv)
     a = torch.randn(2048, 2048, device=DEV, dtype=torch.bfloat16)
     b = torch.randn(2048, 2048, device=DEV, dtype=torch.bfloat16)
+    xi = [cfa.round_bf16(torch.from_numpy(x).to(DEV)) for x in synth.gaussian(1, 4096, 4, 128, 128, 52)]
+    side = torch.cuda.Stream(device=DEV)
     ref_o, ref_l = run()
     ref_o, ref_l = ref_o.clone(), ref_l.clone()
-    for i in range(20):
+    torch.cuda.synchronize()
+    for i in range(200):
         if i % 2:
-            (a @ b).sum()  # a BF16 GEMM between launches (paper Table XII)
+            (a @ b).sum()  # a BF16 GEMM between launches
+        else:
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):  # BF16 attention overlapping the next launch
+                cfa.attn_fwd_causal_bf16(*xi)
         o, l = run()
-        assert torch.equal(o.view(torch.int16), ref_o.view(torch.int16))
-        assert torch.equal(l.view(torch.int32), ref_l.view(torch.int32))
+        assert torch.equal(o.view(torch.int16), ref_o.view(torch.int16)), i
+        assert torch.equal(l.view(torch.int32), ref_l.view(torch.int32)), i
+    torch.cuda.synchronize()
 
 
 def test_every_tile_written():
