@@ -321,33 +321,55 @@ def run_rotate_prepass(torch, cfa, B, H, S, D, warmup, steps, seed=0):
     return out
 
 
-def cpu_baseline(B, H, S, dqk, budget_s=20.0, seed=0):
-    """The oracle's FP8 emulation (mirror mode) timed on host cores over a bounded sample
-    of the headline workload: 32-row groups at seeded positions until ~budget_s of work."""
+def cpu_baseline(B, H, S, dqk, stride=8, seed=0):
+    """The oracle timed on the host cores (a reported baseline, not a target): exact fp64
+    attention (orc_attn_exact) and the FP8 scheme emulation (orc_emulate_fp8, mirror mode)
+    on the same rows of the headline workload, heads {0, H/2, H-1}, every `stride`-th
+    32-row group of each head from a seeded offset (so the causal row lengths, and with them
+    the cost, are sampled evenly); and the tiny configuration B=1 H=1 S=256 in full.
+    Throughput counts the causal half of each row: 2 (i + 1) (d_qk + d_v) FLOP for row i."""
     import oracle
     import synth
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    c = 1.0 / math.sqrt(dqk)
+
+    def legs(qc, kc, vc, dq, dk, dv, groups):
+        rows = oracle.group_rows(groups, 32)
+        f = float(np.sum(2.0 * (rows[:, 2] + 1) * (dqk + 128)))
+        t1 = time.perf_counter()
+        oracle.attn_exact(qc, kc, vc, dtype="fp8", c=c, dq=dq, dk=dk, dv=dv, rows=rows)
+        t_ex = time.perf_counter() - t1
+        t1 = time.perf_counter()
+        oracle.emulate_fp8(qc, kc, vc, dq=dq, dk=dk, dv=dv, c=c, groups=groups)
+        t_em = time.perf_counter() - t1
+        return f, t_ex, t_em, len(rows)
+
+    # tiny configuration, every row
+    q, k, v = synth.gaussian(1, 256, 1, dqk, 128, seed)
+    (qc, dq), (kc, dk), (vc, dv) = (oracle.quantize_e4m3(x) for x in (q, k, v))
+    tg = np.array([(0, 0, r) for r in range(0, 256, 32)], dtype=np.int64)
+    f1, t1_ex, t1_em, _ = legs(qc, kc, vc, dq, dk, dv, tg)
+    # headline workload, head subset
     q, k, v = synth.gaussian(B, S, H, dqk, 128, seed)
     t0 = time.time()
     (qc, dq), (kc, dk), (vc, dv) = (oracle.quantize_e4m3(x) for x in (q, k, v))
+    t_quant = time.time() - t0
     del q, k, v
-    rng = np.random.default_rng(seed + 1)
-    c = 1.0 / math.sqrt(dqk)
-    total_f, total_t, ngroups = 0.0, 0.0, 0
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    log(f"cpu baseline: oracle quantised inputs in {time.time() - t0:.1f} s, sampling for ~{budget_s:.0f} s")
-    while total_t < budget_s and ngroups < 4096:
-        n = threads
-        groups = np.stack([rng.integers(0, B, n), rng.integers(0, H, n), rng.integers(0, S // 32, n) * 32], axis=1)
-        t1 = time.perf_counter()
-        oracle.emulate_fp8(qc, kc, vc, dq=dq, dk=dk, dv=dv, c=c, groups=groups.astype(np.int64))
-        total_t += time.perf_counter() - t1
-        rows = oracle.group_rows(groups, 32)
-        total_f += float(np.sum(2.0 * (rows[:, 2] + 1) * (dqk + 128)))
-        ngroups += n
-    return {"value": total_f / total_t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"FP8 scheme emulation (mirror mode) of {ngroups} seeded 32-row groups of the "
-                      f"B={B} H={H} S={S} d={dqk} workload, {total_t:.1f} s of CPU time; F counts the causal "
-                      f"half of each sampled row; host quantisation ({time.time() - t0 - total_t:.1f} s) excluded"}
+    heads = sorted({0, H // 2, H - 1})
+    off = int(np.random.default_rng(seed + 1).integers(stride))
+    groups = np.array([(0, h, 32 * g) for h in heads for g in range(off, S // 32, stride)], dtype=np.int64)
+    log(f"cpu baseline: oracle quantised inputs in {t_quant:.1f} s; {len(groups)} row groups of heads {heads}")
+    f, t_ex, t_em, nrows = legs(qc, kc, vc, dq, dk, dv, groups)
+    sample = (f"heads {heads} of the B={B} H={H} S={S} d={dqk} workload, every {stride}th 32-row group from "
+              f"offset {off} ({nrows} rows, {f:.3e} FLOP of causal work); host quantisation ({t_quant:.1f} s) "
+              f"excluded")
+    return {"value": round(f / t_em / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "FP8 scheme emulation (mirror mode) on " + sample,
+            "fp64_exact": {"value": round(f / t_ex / 1e12, 5), "unit": "TFLOP/s", "seconds": round(t_ex, 2),
+                           "sample": "exact fp64 attention on the same rows"},
+            "emulation_seconds": round(t_em, 2),
+            "tiny_B1_H1_S256_full": {"fp64_exact_ms": round(1e3 * t1_ex, 2), "emulation_ms": round(1e3 * t1_em, 2),
+                                     "flop": f1}}
 
 
 def traffic_entry():
@@ -382,7 +404,8 @@ def main():
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sustained", action="store_true", help="skip the sustained-clock window")
-    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--cpu-stride", type=int, default=8,
+                    help="the CPU baseline samples every n-th 32-row group of three heads")
     ap.add_argument("--line", choices=sorted(LINES),
                     help="time one other configuration alone with --warmup/--steps and print its result "
                          "(for profiler and counter runs)")
@@ -493,7 +516,7 @@ def main():
         result["also"] = also
         result["fp8_over_bf16_speedup_S32768"] = round(head["tflops"] / also["bf16_B1_H32_S32768_d128"]["tflops"], 3)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(B, H, S, D, budget_s=args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(B, H, S, D, stride=args.cpu_stride)
     print(json.dumps(result), flush=True)
 
 
