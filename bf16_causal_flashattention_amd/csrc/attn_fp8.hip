@@ -188,9 +188,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
     }
   }
   const int st_lds = 16 * 64 * wq + (stage_k ? 0 : L::kVBase);
-  // whether this wave has a fifth 64-cell copy round (K: waves 0, 1 of group 0; V: wave 0 of
-  // group 1), for the hand-ordered matrix phase
-  const uint32_t round5 = ((stage_k ? 3u : 1u) >> wq) & 1u;
+  // copy rounds of this wave: those of its 64-cell shares 256 p + 64 wq inside the slot
+  const uint32_t nrounds = (uint32_t)(st_cells - 64 * wq + 255) >> 8;
 
   // row-sum selector (Sec. IV-B3): lane L of the 16x16x128 A operand is all ones
   // iff (L/16)%2 == ((L%16)/4)%2, so every lane receives the sum of its own query.
@@ -349,6 +348,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
         float xt0, xt1;
         v4f b0, b1;
         v8i g0, g1;  // the operand groups, clobbered
+        if constexpr (DQK == 128) {
         asm volatile(
             // wait states before the first copy's scalar base (a compiler reload of it may precede)
             "s_nop 4\n\t"
@@ -494,8 +494,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
             "v_mul_f32 %[t0], %[cp], %[t0]\n\t"
             "v_max_f32 %[t1], %[t1], %[x1]\n\t"
             "v_mul_f32 %[t1], %[cp], %[t1]\n\t"
-            // the wave's copies of block i+2: four 64-cell rounds, and a fifth for the waves that have one;
-            // these instructions also cover the wait states a VALU read of the last PV results needs
+            // the wave's copies of block i+2: four 64-cell rounds, and up to 1 more for the waves
+            // whose slot share has them (%[nr] rounds in all); these instructions also cover the wait
+            // states a VALU read of the last PV results needs
             "s_mov_b32 m0, %[mb]\n\t"
             "s_nop 0\n\t"
             "global_load_lds_dwordx4 %[a0], %[gs]\n\t"
@@ -508,7 +509,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
             "s_add_u32 m0, %[mb], 12288\n\t"
             "s_nop 0\n\t"
             "global_load_lds_dwordx4 %[a3], %[gs]\n\t"
-            "s_cmp_eq_u32 %[five], 0\n\t"
+            "s_cmp_le_u32 %[nr], 4\n\t"
             "s_cbranch_scc1 1f\n\t"
             "s_add_u32 m0, %[mb], 16384\n\t"
             "s_nop 0\n\t"
@@ -522,8 +523,215 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
             : [kb] "v"(kb), [vb] "v"(vb), [q0] "v"(qop[0]), [q1] "v"(qop[1]), [p0] "v"(pb[0]), [p1] "v"(pb[1]),
               [selw] "v"(selw), [one] "v"(one), [c0] "v"(sc0), [c1] "v"(sc1), [mb] "s"(mb), [gs] "s"(gs),
               [a0] "v"(st_goff[0]), [a1] "v"(st_goff[1]), [a2] "v"(st_goff[2]), [a3] "v"(st_goff[3]),
-              [a4] "v"(st_goff[NR > 4 ? 4 : 0]), [five] "s"(round5), [cp] "s"(cp)
+              [a4] "v"(st_goff[4]), [nr] "s"(nrounds), [cp] "s"(cp)
             : "memory", "scc");
+        } else {
+        asm volatile(
+            // wait states before the first copy's scalar base (a compiler reload of it may precede)
+            "s_nop 4\n\t"
+            "s_mov_b32 %[m0s], m0\n\t"
+            "s_waitcnt lgkmcnt(0)\n\t"
+            // row sums of P(i): the 0/1 selector in group 1, the first K operand read in group 0
+            "v_mov_b32 v248, %[selw]\n\t"
+            "v_mov_b32 v249, %[selw]\n\t"
+            "v_mov_b32 v250, %[selw]\n\t"
+            "v_mov_b32 v251, %[selw]\n\t"
+            "v_mov_b32 v252, %[selw]\n\t"
+            "v_mov_b32 v253, %[selw]\n\t"
+            "v_mov_b32 v254, %[selw]\n\t"
+            "v_mov_b32 v255, %[selw]\n\t"
+            "ds_read_b128 v[240:243], %[kb]\n\t"
+            "ds_read_b128 v[244:247], %[kb] offset:16\n\t"
+            "s_nop 1\n\t"
+            "v_mfma_scale_f32_16x16x128_f8f6f4 %[b0], v[248:255], %[p0], 0, %[one], %[one] op_sel_hi:[0,0,0]\n\t"
+            "v_mfma_scale_f32_16x16x128_f8f6f4 %[b1], v[248:255], %[p1], 0, %[one], %[one] op_sel_hi:[0,0,0]\n\t"
+            // S^T(i+1) = K Q^T: sub-tile u, 64-wide chunk c, chunk-outer; each operand read two MFMAs ahead
+            "ds_read_b128 v[248:251], %[kb] offset:6656\n\t"
+            "ds_read_b128 v[252:255], %[kb] offset:6672\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 v[176:191], v[240:247], %[q0], 0, %[one], %[one] op_sel_hi:[0,0,0]\n\t"
+            "ds_read_b128 v[240:243], %[kb] offset:13312\n\t"
+            "ds_read_b128 v[244:247], %[kb] offset:13328\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 v[192:207], v[248:255], %[q0], 0, %[one], %[one] op_sel_hi:[0,0,0]\n\t"
+            "ds_read_b128 v[248:251], %[kb] offset:19968\n\t"
+            "ds_read_b128 v[252:255], %[kb] offset:19984\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 v[208:223], v[240:247], %[q0], 0, %[one], %[one] op_sel_hi:[0,0,0]\n\t"
+            "ds_read_b128 v[240:243], %[kb] offset:64\n\t"
+            "ds_read_b128 v[244:247], %[kb] offset:80\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 v[224:239], v[248:255], %[q0], 0, %[one], %[one] op_sel_hi:[0,0,0]\n\t"
+            "ds_read_b128 v[248:251], %[kb] offset:6720\n\t"
+            "ds_read_b128 v[252:255], %[kb] offset:6736\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 v[176:191], v[240:247], %[q1], v[176:191], %[one], %[one] op_sel_hi:[0,0,0]\n\t"
+            "ds_read_b128 v[240:243], %[kb] offset:13376\n\t"
+            "ds_read_b128 v[244:247], %[kb] offset:13392\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 v[192:207], v[248:255], %[q1], v[192:207], %[one], %[one] op_sel_hi:[0,0,0]\n\t"
+            "ds_read_b128 v[248:251], %[kb] offset:20032\n\t"
+            "ds_read_b128 v[252:255], %[kb] offset:20048\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 v[208:223], v[240:247], %[q1], v[208:223], %[one], %[one] op_sel_hi:[0,0,0]\n\t"
+            "ds_read_b128 v[240:243], %[kb] offset:128\n\t"
+            "ds_read_b128 v[244:247], %[kb] offset:144\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 v[224:239], v[248:255], %[q1], v[224:239], %[one], %[one] op_sel_hi:[0,0,0]\n\t"
+            "ds_read_b128 v[248:251], %[kb] offset:6784\n\t"
+            "ds_read_b128 v[252:255], %[kb] offset:6800\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 v[176:191], v[240:247], %[q2], v[176:191], %[one], %[one] op_sel_hi:[0,0,0]\n\t"
+            "ds_read_b128 v[240:243], %[kb] offset:13440\n\t"
+            "ds_read_b128 v[244:247], %[kb] offset:13456\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 v[192:207], v[248:255], %[q2], v[192:207], %[one], %[one] op_sel_hi:[0,0,0]\n\t"
+            "ds_read_b128 v[248:251], %[kb] offset:20096\n\t"
+            "ds_read_b128 v[252:255], %[kb] offset:20112\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 v[208:223], v[240:247], %[q2], v[208:223], %[one], %[one] op_sel_hi:[0,0,0]\n\t"
+            // the first two V^T operands of PV(i), four transpose reads each
+            "ds_read_b64_tr_b8 v[240:241], %[vb]\n\t"
+            "ds_read_b64_tr_b8 v[242:243], %[vb] offset:256\n\t"
+            "ds_read_b64_tr_b8 v[244:245], %[vb] offset:4224\n\t"
+            "ds_read_b64_tr_b8 v[246:247], %[vb] offset:4480\n\t"
+            "s_waitcnt lgkmcnt(4)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 v[224:239], v[248:255], %[q2], v[224:239], %[one], %[one] op_sel_hi:[0,0,0]\n\t"
+            "ds_read_b64_tr_b8 v[248:249], %[vb] offset:32\n\t"
+            "ds_read_b64_tr_b8 v[250:251], %[vb] offset:288\n\t"
+            "ds_read_b64_tr_b8 v[252:253], %[vb] offset:4256\n\t"
+            "ds_read_b64_tr_b8 v[254:255], %[vb] offset:4512\n\t"
+            "s_waitcnt lgkmcnt(4)\n\t"
+            // O^T += V^T(i) P^T(i) with the 2^-o scale of each 64-key block; between these MFMAs the maxima
+            // of the two 64-key blocks of S(i+1), each a v_max3 chain over a lane's 32 scores of the block
+            // (the scores were written five or more MFMAs earlier)
+            "v_mfma_scale_f32_32x32x64_f8f6f4 %[o0], v[240:247], %[p0], %[o0], %[one], %[c0] op_sel_hi:[0,0,0]\n\t"
+            "ds_read_b64_tr_b8 v[240:241], %[vb] offset:64\n\t"
+            "ds_read_b64_tr_b8 v[242:243], %[vb] offset:320\n\t"
+            "ds_read_b64_tr_b8 v[244:245], %[vb] offset:4288\n\t"
+            "ds_read_b64_tr_b8 v[246:247], %[vb] offset:4544\n\t"
+            "s_waitcnt lgkmcnt(4)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 %[o1], v[248:255], %[p0], %[o1], %[one], %[c0] op_sel_hi:[0,0,0]\n\t"
+            "ds_read_b64_tr_b8 v[248:249], %[vb] offset:96\n\t"
+            "ds_read_b64_tr_b8 v[250:251], %[vb] offset:352\n\t"
+            "ds_read_b64_tr_b8 v[252:253], %[vb] offset:4320\n\t"
+            "ds_read_b64_tr_b8 v[254:255], %[vb] offset:4576\n\t"
+            "v_max3_f32 %[t0], v176, v177, v178\n\t"
+            "v_max3_f32 %[t0], %[t0], v179, v180\n\t"
+            "v_max3_f32 %[t0], %[t0], v181, v182\n\t"
+            "v_max3_f32 %[t0], %[t0], v183, v184\n\t"
+            "v_max3_f32 %[t0], %[t0], v185, v186\n\t"
+            "v_max3_f32 %[t0], %[t0], v187, v188\n\t"
+            "s_waitcnt lgkmcnt(4)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 %[o2], v[240:247], %[p0], %[o2], %[one], %[c0] op_sel_hi:[0,0,0]\n\t"
+            "ds_read_b64_tr_b8 v[240:241], %[vb] offset:8448\n\t"
+            "ds_read_b64_tr_b8 v[242:243], %[vb] offset:8704\n\t"
+            "ds_read_b64_tr_b8 v[244:245], %[vb] offset:12672\n\t"
+            "ds_read_b64_tr_b8 v[246:247], %[vb] offset:12928\n\t"
+            "v_max3_f32 %[t0], %[t0], v189, v190\n\t"
+            "v_max3_f32 %[t0], %[t0], v191, v192\n\t"
+            "v_max3_f32 %[t0], %[t0], v193, v194\n\t"
+            "v_max3_f32 %[t0], %[t0], v195, v196\n\t"
+            "v_max3_f32 %[t0], %[t0], v197, v198\n\t"
+            "s_waitcnt lgkmcnt(4)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 %[o3], v[248:255], %[p0], %[o3], %[one], %[c0] op_sel_hi:[0,0,0]\n\t"
+            "ds_read_b64_tr_b8 v[248:249], %[vb] offset:8480\n\t"
+            "ds_read_b64_tr_b8 v[250:251], %[vb] offset:8736\n\t"
+            "ds_read_b64_tr_b8 v[252:253], %[vb] offset:12704\n\t"
+            "ds_read_b64_tr_b8 v[254:255], %[vb] offset:12960\n\t"
+            "v_max3_f32 %[t0], %[t0], v199, v200\n\t"
+            "v_max3_f32 %[t0], %[t0], v201, v202\n\t"
+            "v_max3_f32 %[t0], %[t0], v203, v204\n\t"
+            "v_max3_f32 %[t0], %[t0], v205, v206\n\t"
+            "v_max_f32 %[t0], %[t0], v207\n\t"
+            "s_waitcnt lgkmcnt(4)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 %[o0], v[240:247], %[p1], %[o0], %[one], %[c1] op_sel_hi:[0,0,0]\n\t"
+            "ds_read_b64_tr_b8 v[240:241], %[vb] offset:8512\n\t"
+            "ds_read_b64_tr_b8 v[242:243], %[vb] offset:8768\n\t"
+            "ds_read_b64_tr_b8 v[244:245], %[vb] offset:12736\n\t"
+            "ds_read_b64_tr_b8 v[246:247], %[vb] offset:12992\n\t"
+            "v_max3_f32 %[t1], v208, v209, v210\n\t"
+            "v_max3_f32 %[t1], %[t1], v211, v212\n\t"
+            "v_max3_f32 %[t1], %[t1], v213, v214\n\t"
+            "v_max3_f32 %[t1], %[t1], v215, v216\n\t"
+            "v_max3_f32 %[t1], %[t1], v217, v218\n\t"
+            "v_max3_f32 %[t1], %[t1], v219, v220\n\t"
+            "s_waitcnt lgkmcnt(4)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 %[o1], v[248:255], %[p1], %[o1], %[one], %[c1] op_sel_hi:[0,0,0]\n\t"
+            "ds_read_b64_tr_b8 v[248:249], %[vb] offset:8544\n\t"
+            "ds_read_b64_tr_b8 v[250:251], %[vb] offset:8800\n\t"
+            "ds_read_b64_tr_b8 v[252:253], %[vb] offset:12768\n\t"
+            "ds_read_b64_tr_b8 v[254:255], %[vb] offset:13024\n\t"
+            "v_max3_f32 %[t1], %[t1], v221, v222\n\t"
+            "v_max3_f32 %[t1], %[t1], v223, v224\n\t"
+            "v_max3_f32 %[t1], %[t1], v225, v226\n\t"
+            "v_max3_f32 %[t1], %[t1], v227, v228\n\t"
+            "v_max3_f32 %[t1], %[t1], v229, v230\n\t"
+            "s_waitcnt lgkmcnt(4)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 %[o2], v[240:247], %[p1], %[o2], %[one], %[c1] op_sel_hi:[0,0,0]\n\t"
+            "v_max3_f32 %[t1], %[t1], v231, v232\n\t"
+            "v_max3_f32 %[t1], %[t1], v233, v234\n\t"
+            "v_max3_f32 %[t1], %[t1], v235, v236\n\t"
+            "v_max3_f32 %[t1], %[t1], v237, v238\n\t"
+            "v_max_f32 %[t1], %[t1], v239\n\t"
+            "s_waitcnt lgkmcnt(0)\n\t"
+            "v_mfma_scale_f32_32x32x64_f8f6f4 %[o3], v[248:255], %[p1], %[o3], %[one], %[c1] op_sel_hi:[0,0,0]\n\t"
+            // the two lanes of a query hold keys 16 hh + r: combine them, then scale to base-2 units
+            "v_mov_b32 %[x0], %[t0]\n\t"
+            "v_mov_b32 %[x1], %[t1]\n\t"
+            "s_nop 1\n\t"
+            "v_permlane32_swap_b32 %[t0], %[x0]\n\t"
+            "v_permlane32_swap_b32 %[t1], %[x1]\n\t"
+            "s_nop 1\n\t"
+            "v_max_f32 %[t0], %[t0], %[x0]\n\t"
+            "v_mul_f32 %[t0], %[cp], %[t0]\n\t"
+            "v_max_f32 %[t1], %[t1], %[x1]\n\t"
+            "v_mul_f32 %[t1], %[cp], %[t1]\n\t"
+            // the wave's copies of block i+2: four 64-cell rounds, and up to 3 more for the waves
+            // whose slot share has them (%[nr] rounds in all); these instructions also cover the wait
+            // states a VALU read of the last PV results needs
+            "s_mov_b32 m0, %[mb]\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %[a0], %[gs]\n\t"
+            "s_add_u32 m0, %[mb], 4096\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %[a1], %[gs]\n\t"
+            "s_add_u32 m0, %[mb], 8192\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %[a2], %[gs]\n\t"
+            "s_add_u32 m0, %[mb], 12288\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %[a3], %[gs]\n\t"
+            "s_cmp_le_u32 %[nr], 4\n\t"
+            "s_cbranch_scc1 1f\n\t"
+            "s_add_u32 m0, %[mb], 16384\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %[a4], %[gs]\n\t"
+            "1:\n\t"
+            "s_cmp_le_u32 %[nr], 5\n\t"
+            "s_cbranch_scc1 1f\n\t"
+            "s_add_u32 m0, %[mb], 20480\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %[a5], %[gs]\n\t"
+            "1:\n\t"
+            "s_cmp_le_u32 %[nr], 6\n\t"
+            "s_cbranch_scc1 1f\n\t"
+            "s_add_u32 m0, %[mb], 24576\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %[a6], %[gs]\n\t"
+            "1:\n\t"
+            "s_mov_b32 m0, %[m0s]\n\t"
+            : "=&{v[176:191]}"(sacc[0]), "=&{v[192:207]}"(sacc[1]), "=&{v[208:223]}"(sacc[2]),
+              "=&{v[224:239]}"(sacc[3]), [t0] "=&v"(bmx[0]), [t1] "=&v"(bmx[1]), [x0] "=&v"(xt0), [x1] "=&v"(xt1),
+              [o0] "+v"(oacc[0]), [o1] "+v"(oacc[1]), [o2] "+v"(oacc[2]), [o3] "+v"(oacc[3]),
+              [b0] "=&v"(b0), [b1] "=&v"(b1), "=&{v[240:247]}"(g0), "=&{v[248:255]}"(g1), [m0s] "=&s"(m0s)
+            : [kb] "v"(kb), [vb] "v"(vb), [q0] "v"(qop[0]), [q1] "v"(qop[1]), [q2] "v"(qop[KC - 1]),
+              [p0] "v"(pb[0]), [p1] "v"(pb[1]), [selw] "v"(selw), [one] "v"(one), [c0] "v"(sc0), [c1] "v"(sc1),
+              [mb] "s"(mb), [gs] "s"(gs), [a0] "v"(st_goff[0]), [a1] "v"(st_goff[1]), [a2] "v"(st_goff[2]),
+              [a3] "v"(st_goff[3]), [a4] "v"(st_goff[4]), [a5] "v"(st_goff[NR > 5 ? 5 : 4]),
+              [a6] "v"(st_goff[NR > 6 ? 6 : 4]), [nr] "s"(nrounds), [cp] "s"(cp)
+            : "memory", "scc");
+        }
         (void)g0;
         (void)g1;
         (void)xt0;
@@ -664,7 +872,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
         // -------------------------------------------------------------- M_i
         __builtin_amdgcn_s_setprio(1);
         const bool live_i = live(i), live_n = (i + 1 < nb) && live(i + 1);
-        if constexpr (DQK == 128 && !VT) {
+        if constexpr (!VT) {
           // every wave runs the whole stream: a block the causal mask hides from all rows of the
           // wave has zero codes (set in the softmax phase), so its PV and row sums add 0, and the
           // scores of a dead or missing next block (its K slot holds an earlier block, in
@@ -689,7 +897,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
         __builtin_amdgcn_s_setprio(0);
         if (live_n) {
           dump_scores(i + 1);
-          if (DQK == 128 && !VT && (i + 1) * kBlockKeys + kBlockKeys - 1 <= row0) {
+          if (!VT && (i + 1) * kBlockKeys + kBlockKeys - 1 <= row0) {
             // below the diagonal for every row of the wave: the matrix phase took the maxima
             bm[0] = bmx[0];
             bm[1] = bmx[1];
@@ -698,14 +906,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
           }
           decide(false);
           codes(i + 1);
-        } else if constexpr (DQK == 128 && !VT) {
+        } else if constexpr (!VT) {
 #pragma unroll
           for (int n = 0; n < 2; ++n) {
             pb[n] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
             o_cur[n] = 0;
           }
         }
-        if ((DQK == 128 && !VT) || i + 2 < nb) wait_dma();
+        if (!VT || i + 2 < nb) wait_dma();
         lds_barrier();
       }
       if (grp == 0) lds_barrier();
