@@ -197,19 +197,21 @@ def sustained_window(torch, fn, F, chunk_s=0.5, window_s=4.0, max_warm_s=6.0):
 
 
 def run_fp8(torch, cfa, kind, synth_fn, B, H, S, dqk, warmup, steps, seed=0, sustained_reps=0,
-            v_channel_major=False):
+            v_channel_major=False, softmax_scale=None):
     """FP8 attention through the basic entry point, or with v_channel_major through the entry
-    point that takes V as [B, H, 128, S] (the transposed copy is made before the timing)."""
+    point that takes V as [B, H, 128, S] (the transposed copy is made before the timing).
+    softmax_scale None means 1/sqrt(d_qk)."""
     log(f"{kind} B={B} H={H} S={S} d_qk={dqk}: generating inputs")
     tens, codes, ds, prep = prep_fp8(torch, cfa, synth_fn, B, S, H, dqk, 128, seed)
     qg, kg, vg = codes
     out = torch.empty((B, S, H, 128), dtype=torch.bfloat16, device="cuda:0")
     lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda:0")
     entry = cfa.attn_fwd_causal_fp8 if dqk == 128 else cfa.attn_fwd_causal_mla
-    fn = lambda: entry(qg, kg, vg, ds[0], ds[1], ds[2], out=out, lse=lse)
+    fn = lambda: entry(qg, kg, vg, ds[0], ds[1], ds[2], softmax_scale=softmax_scale, out=out, lse=lse)
     if v_channel_major:
         vt = vg.view(torch.uint8).permute(0, 2, 3, 1).contiguous()
-        fn = lambda: cfa.attn_fwd_causal_fp8_vt(qg, kg, vt, ds[0], ds[1], ds[2], out=out, lse=lse)
+        fn = lambda: cfa.attn_fwd_causal_fp8_vt(qg, kg, vt, ds[0], ds[1], ds[2], softmax_scale=softmax_scale,
+                                                out=out, lse=lse)
     ms = time_launches(torch, fn, warmup, steps)
     prep_ms = time_launches(torch, prep, 2, 5)
     log(f"{kind} B={B} H={H} S={S} d_qk={dqk}: {ms:.4f} ms/launch")
@@ -383,6 +385,22 @@ def traffic_entry():
         return None
 
 
+def act_2sigma(B, S, H, dqk, dv, seed):
+    """The activation-like input with its sink at 2 sigma instead of 12: with the softmax scale
+    ACT_2SIGMA_SCALE the non-sink logits have standard deviation 2.5 and the sink's logit is 5,
+    so the probabilities spread over many keys instead of sitting on the sink."""
+    import synth
+    return synth.activation_like(B, S, H, dqk, dv, seed, sink_sigmas=2.0)
+
+
+def _act_2sigma_scale():
+    import synth
+    return 2.5 / synth.activation_sigma_raw(128)
+
+
+ACT_2SIGMA_SCALE = _act_2sigma_scale()
+
+
 # single configurations for --line: (torch, cfa, synth, warmup, steps) -> result of the run_* helper
 LINES = {
     "bf16": lambda t, c, sy, w, n: run_bf16(t, c, 1, 32, 32768, w, n),
@@ -391,6 +409,8 @@ LINES = {
     "bf16_mla": lambda t, c, sy, w, n: run_bf16(t, c, 1, 16, 32768, w, n, dqk=192),
     "gqa": lambda t, c, sy, w, n: run_fp8_ex(t, c, 1, 32, 8, 32768, 128, c.P_LEAN, w, n),
     "act": lambda t, c, sy, w, n: run_fp8(t, c, "fp8", sy.activation_like, 1, 32, 16384, 128, w, n),
+    "act_2sigma": lambda t, c, sy, w, n: run_fp8(t, c, "fp8", act_2sigma, 1, 32, 16384, 128, w, n,
+                                                 softmax_scale=ACT_2SIGMA_SCALE),
     "fp8_vt": lambda t, c, sy, w, n: run_fp8(t, c, "fp8", sy.gaussian, 1, 32, 32768, 128, w, n, v_channel_major=True),
     "fp8_4k": lambda t, c, sy, w, n: run_fp8(t, c, "fp8", sy.gaussian, 1, 32, 4096, 128, w, n),
 }
@@ -501,7 +521,12 @@ def main():
         also["fp8_gqa_B1_H32_Hkv8_S32768_d128"] = {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4),
                                                     "pct_fp8_peak": round(100 * r["tflops"] / PEAK_TFLOPS["fp8"], 2)}
         r = run_fp8(torch, cfa, "fp8", synth.activation_like, 1, 32, 16384, 128, wb, sb)
-        also["fp8_activation_like_B1_H32_S16384_d128"] = {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4)}
+        also["fp8_activation_like_B1_H32_S16384_d128"] = {"tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4),
+                                                           "note": "12-sigma sink: every row's softmax is one-hot"}
+        r = run_fp8(torch, cfa, "fp8", act_2sigma, 1, 32, 16384, 128, wb, sb, softmax_scale=ACT_2SIGMA_SCALE)
+        also["fp8_activation_like_2sigma_B1_H32_S16384_d128"] = {
+            "tflops": round(r["tflops"], 2), "ms": round(r["ms"], 4),
+            "note": "2-sigma sink, softmax scale 2.5/sigma_raw: logit sd 2.5, rows not one-hot"}
         # the paper's own timing inputs, N(0, 0.1^2): nearly uniform probabilities, so other
         # operand bits switch and the clock differs (Sec. III-C)
         gauss01 = lambda B_, S_, H_, dqk_, dv_, seed_: synth.gaussian(B_, S_, H_, dqk_, dv_, seed_, std=0.1)

@@ -211,6 +211,12 @@ def chunk_error_bound(qc, kc):
     return MFMA_ERR_PER_CHUNK * out.reshape(B * H * S, S)
 
 
+def _max_ratio(err, bound):
+    """Largest err/bound; an element with a zero bound counts 0 if its error is 0, else inf."""
+    r = np.divide(err, bound, out=np.where(err > 0, np.inf, 0.0), where=bound > 0)
+    return float(np.max(r))
+
+
 def check_fp8_on_gpu_scores(qg, kg, vg, dq, dk, dv, c, p_mode, ref=None, report=None):
     """Complete check of one FP8 call at a size the debug hook allows (B*H*S^2 <= 2^28):
 
@@ -264,7 +270,7 @@ def check_fp8_on_gpu_scores(qg, kg, vg, dq, dk, dv, c, p_mode, ref=None, report=
     l_bound = l_bound + 2.0 ** -21 * np.abs(emu["lse"])  # the kernel forms the LSE in fp32
     res = {"score_err_over_bound": ratio, "code_mismatch_in_band": int(mism.sum()),
            "maxabs": float(np.max(err)), "rms": rms_rel(got, emu["out"]), "lse": float(np.max(lerr)),
-           "maxabs_over_bound": float(np.max(err / o_bound)), "lse_over_bound": float(np.max(lerr / l_bound))}
+           "maxabs_over_bound": _max_ratio(err, o_bound), "lse_over_bound": _max_ratio(lerr, l_bound)}
     print("GPU-SCORES", res, flush=True)
     if report is not None:
         report.update(res)

@@ -14,8 +14,9 @@ import torch
 import bf16_causal_flashattention_amd as cfa
 import oracle
 import synth
-from gpu_util import (DEV, LSE_EMU_NATS, LSE_FP64_NATS, TOL_EMU_MAXABS, TOL_EMU_RMS, TOL_FP64_RMS_BF16,
-                      TOL_FP64_RMS_FP8, gpu_rows, lse_rows, rms_rel, sample_groups, snr_db)
+from gpu_util import (DEV, LSE_EMU_NATS, LSE_FP64_NATS, MFMA_ERR_PER_CHUNK, TOL_EMU_MAXABS, TOL_EMU_RMS,
+                      TOL_FP64_RMS_BF16, TOL_FP64_RMS_FP8, check_fp8_on_gpu_scores, gpu_rows, lse_rows, rms_rel,
+                      sample_groups, snr_db)
 
 pytestmark = pytest.mark.gpu
 
@@ -24,7 +25,8 @@ def _case(*a):
     print("CASE", *a, flush=True)
 
 
-def _fp8_full(gen, B, H, S, dqk, exact_p, seed, n_groups):
+def _fp8_full(gen, B, H, S, dqk, exact_p, seed, n_groups, scale=None, keep=None):
+    """keep: a list that receives (codes q, k, v as uint8, descales, out, lse) of the call."""
     q, k, v = gen(B, S, H, dqk, 128, seed)
     gpu = []
     for x in (q, k, v):
@@ -37,7 +39,7 @@ def _fp8_full(gen, B, H, S, dqk, exact_p, seed, n_groups):
         assert gd == hd
         assert np.array_equal(gc.view(torch.uint8).cpu().numpy(), hc)  # a0 bit-exact at full size
     (qg, dq), (kg, dk), (vg, dv) = gpu
-    c = 1.0 / math.sqrt(dqk)
+    c = 1.0 / math.sqrt(dqk) if scale is None else scale
     out = torch.full((B, S, H, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
     lse = torch.full((B, H, S), float("nan"), dtype=torch.float32, device=DEV)
     entry = cfa.attn_fwd_causal_fp8 if dqk == 128 else cfa.attn_fwd_causal_mla
@@ -54,8 +56,10 @@ def _fp8_full(gen, B, H, S, dqk, exact_p, seed, n_groups):
     res = {"emu_maxabs": float(np.max(np.abs(got - emu["out"]))), "emu_rms": rms_rel(got, emu["out"]),
            "fp64_rms": rms_rel(got, ex), "fp64_maxabs": float(np.max(np.abs(got - ex))),
            "fp64_snr_db": snr_db(got, ex), "lse_emu": float(np.max(np.abs(glse - emu["lse"]))),
-           "lse_fp64": float(np.max(np.abs(glse - ex_lse)))}
+           "lse_fp64": float(np.max(np.abs(glse - ex_lse))), "lse_absmax": float(np.max(np.abs(glse)))}
     print("RESULT", res, flush=True)
+    if keep is not None:
+        keep.extend([qg.view(torch.uint8), kg.view(torch.uint8), vg.view(torch.uint8), (dq, dk, dv), out, lse])
     del out, lse, gpu
     torch.cuda.empty_cache()
     return res
@@ -83,6 +87,51 @@ def test_c5_activation_like_b1_h32_s16384():
     assert r["emu_maxabs"] <= TOL_EMU_MAXABS and r["emu_rms"] <= TOL_EMU_RMS
     assert r["fp64_rms"] <= TOL_FP64_RMS_FP8
     assert r["lse_emu"] <= LSE_EMU_NATS and r["lse_fp64"] <= LSE_FP64_NATS
+
+
+def test_c5_activation_like_2sigma_b1_h32_s16384():
+    """The activation-like input with a 2-sigma sink and softmax scale 2.5/sigma_raw, where the
+    rows are not one-hot: the non-sink logits have standard deviation 2.5, the sink's is 5.
+
+    Here the P codes of the leading keys often sit near a rounding boundary, so an MFMA score
+    error can move a code by one step, and the element-wise result is not unique against the
+    emulation on exact scores.  Two checks instead:
+    * the first 1024 rows of heads 0-7: causal row i depends on keys 0..i only, so the
+      full-size launch must equal, bit for bit, a launch on the 1024-key prefix, and that
+      launch passes the complete check on the kernel's own scores (scores within the MFMA
+      bound, the same exponents and codes, O and LSE within the gates);
+    * sampled 32-row groups across the sequence: RMS gates against the emulation and exact
+      fp64 attention, and the LSE against the emulation within the bound that the lean-P
+      encoding gives.  A key enters the row sum as 2^(round(y)/8) with y = 8 c' s + const, and
+      LSE = m + log2(row sum) up to constants, so the running maximum cancels; per key the two
+      sides then differ by (dy + r' - r)/8 in log2 units, with dy the score error in steps of y
+      and r, r' the two rounding errors (each at most 1/2).  The LSE, a log-sum of these
+      weights, differs by at most ln 2 (1 + max dy) / 8 nats."""
+    _case("C5 FP8 activation-like, 2-sigma sink, B1 H32 S16384 d128")
+    B, H, S, D = 1, 32, 16384, 128
+    c = 2.5 / synth.activation_sigma_raw(D)
+    gen = lambda *a: synth.activation_like(*a, sink_sigmas=2.0)
+    kept = []
+    r = _fp8_full(gen, B, H, S, D, False, 13, 12, scale=c, keep=kept)
+    assert r["emu_rms"] <= TOL_EMU_RMS and r["fp64_rms"] <= TOL_FP64_RMS_FP8
+    qg, kg, vg, (dq, dk, dv), out, lse = kept
+    # the largest possible score error, in steps of y (MFMA bound of each 64-channel chunk)
+    t = np.abs(oracle.e4m3_table())
+    Q, K = t[qg.cpu().numpy()], t[kg.cpu().numpy()]
+    qmax, kmax = Q.max(axis=(0, 1, 2)), K.max(axis=(0, 1, 2))
+    raw_err = sum(MFMA_ERR_PER_CHUNK * float(np.max(qmax[e:e + 64] * kmax[e:e + 64])) for e in range(0, D, 64))
+    y_err = 8 * c * dq * dk * math.log2(math.e) * raw_err
+    print("max score error in steps of y", y_err, flush=True)
+    assert r["lse_emu"] <= math.log(2.0) * (1.0 + y_err) / 8 + 2.0 ** -21 * r["lse_absmax"]  # fp32 LSE
+    # the prefix: bit for bit against a launch on the first 1024 keys, which is checked completely
+    Sp, Hp = 1024, 8
+    qp, kp, vp = (x[:, :Sp, :Hp].contiguous() for x in (qg, kg, vg))
+    ref = (out[:, :Sp, :Hp], lse[:, :Hp, :Sp])
+    mine = cfa.attn_fwd_causal_fp8_ex(qp, kp, vp, dq, dk, dv, softmax_scale=c, p_mode=cfa.P_LEAN)
+    torch.cuda.synchronize()
+    assert torch.equal(mine[0].view(torch.int16), ref[0].contiguous().view(torch.int16))
+    assert torch.equal(mine[1], ref[1])
+    check_fp8_on_gpu_scores(qp, kp, vp, dq, dk, dv, c, cfa.P_LEAN, ref=ref)
 
 
 @pytest.mark.parametrize("S", [4096, 8192, 16384, 32768])
