@@ -122,6 +122,27 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const lds_void_t*)p;
 }
 
+// One 64-cell copy round from global memory into LDS, in the form the hand-ordered matrix
+// phase uses: a wave-uniform 64-bit base in scalar registers plus each lane's 32-bit offset,
+// with M0 = the round's LDS base (saved and restored).  With a per-lane 64-bit address the
+// compiler keeps one address pair per round, spills them, and reloads them with a wait for
+// every load in flight before each copy.  Five wait states come first in case the compiler
+// has just written a scalar operand from a vector instruction (a spill reload), and one after
+// the M0 write.
+__device__ __forceinline__ void copy_round(uint64_t gs, uint32_t m, uint32_t off) {
+  int t;
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b32 %[t], m0\n\t"
+      "s_mov_b32 m0, %[m]\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %[o], %[gs]\n\t"
+      "s_mov_b32 m0, %[t]"
+      : [t] "=&s"(t)
+      : [m] "s"(m), [o] "v"(off), [gs] "s"(gs)
+      : "memory");
+}
+
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -221,11 +242,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
 
       // DMA of block blk: K by group 0 into slot blk % 2, V by group 1 into slot blk % 3
       auto stage = [&](int blk) {
-        const uint8_t* src = st_head + blk * st_bstep;
-        uint8_t* dst = smem + st_lds + (stage_k ? (blk & 1) * L::kKSlot : (blk % 3) * L::kVSlot);
+        const uint64_t gs = (uint64_t)(uintptr_t)(st_head + blk * st_bstep);  // wave-uniform
+        const uint32_t mb = __builtin_amdgcn_readfirstlane(
+            lds_addr(smem) + st_lds + (stage_k ? (blk & 1) * L::kKSlot : (blk % 3) * L::kVSlot));
 #pragma unroll
         for (int p = 0; p < NR; ++p)
-          if (256 * p + 64 * wq < st_cells) dma16(src + st_goff[p], dst + 4096 * p);
+          if (256 * p + 64 * wq < st_cells) copy_round(gs, mb + 4096 * p, st_goff[p]);
       };
 
       // ---------------------------------------------------------------- per-wave state
@@ -849,11 +871,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
       };
 
       // ---------------------------------------------------------------- prologue
-      // K(0), K(1) by group 0 and V(0), V(1) by group 1
+      // K(0), K(1) by group 0 and V(0), V(1) by group 1.  Only the Q rows and block 0 are
+      // waited for here: block 1 streams in under the first two phases and each wave waits
+      // for its share at the end of its S_pro (K(1) is first read in M_0, V(1) in M_1), so a
+      // tile starts after one block's copies instead of two.
       stage(0);
-      stage(1);
       wait_dma();
       lds_barrier();
+      stage(1);
       if (grp == 1) lds_barrier();  // group 1 runs one phase behind
 
       // M_pro
@@ -866,6 +891,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
         decide(true);
         codes(0);
       }
+      wait_dma();
       lds_barrier();
 
       for (int i = 0; i < nb; ++i) {
