@@ -162,10 +162,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
   const v16f zero16 = {};
   const float cp = a.cp;
 
+  // (b, h, j) of the workgroup's first item; later items follow by scalar increments, so the
+  // loop holds no division (whose reciprocals the compiler would keep in vector registers)
+  int b, h, j;
+  decode_item(work.first, H, sch.P, b, h, j);
+  int hk = h / a.G, hg = h - hk * a.G;  // key/value head of query head h, and h's place in its group
   for (int64_t item = work.first; item < work.end; item += work.step) {
-    int b, h, j;
-    decode_item(item, H, sch.P, b, h, j);
-    const int hk = h / a.G;  // key/value head of query head h
     const uint8_t* qbh = (const uint8_t*)a.q + b * a.mq.sb + h * a.mq.sh;
     const uint8_t* st_head = stage_k ? (const uint8_t*)a.k + b * a.mk.sb + hk * a.mk.sh
                                      : (const uint8_t*)a.v + b * a.mv.sb + hk * a.mv.sh;
@@ -180,7 +182,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
       const int qrow = row0 + l32;
       const int nb = 4 * tile + 4;  // 64-key blocks
 
-      auto stage = [&](int blk) {  // DMA of block blk: K into slot blk % 2, V into slot blk % 3
+      // DMA of block blk: K into slot blk % 2, V into slot blk % 3.  The prologue copies go
+      // through a scalar base (copy_round: no per-lane 64-bit addresses to keep, spill and reload
+      // at every tile start); the loop's copies, one block per 64 keys, keep the builtin, whose
+      // per-lane address costs less there than the asm round's fixed wait states and M0 handling
+      // (measured 0.5-1% at 16K-32K)
+      auto stage = [&](int blk) {
+        const uint64_t gs = (uint64_t)(uintptr_t)(st_head + (int64_t)(blk * kBlk) * st_rs);  // wave-uniform
+        const uint32_t mb = __builtin_amdgcn_readfirstlane(
+            lds_addr(smem) + st_lds + (stage_k ? (blk & 1) * kKSlot : (blk % 3) * kVSlot));
+#pragma unroll
+        for (int p = 0; p < kRounds; ++p)
+          if (256 * p + 64 * wq < st_cells) copy_round(gs, mb + 4096 * p, st_goff[p]);
+      };
+      auto stage_loop = [&](int blk) {
         const uint8_t* src = st_head + (int64_t)(blk * kBlk) * st_rs;
         uint8_t* dst = smem + st_lds + (stage_k ? (blk & 1) * kKSlot : (blk % 3) * kVSlot);
 #pragma unroll
@@ -190,7 +205,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
 
       v4i qop[QM];  // Q^T operand: lane holds Q[qrow][16m + 8hh .. +8]
       {
-        const uint8_t* qp = qbh + (int64_t)qrow * a.mq.ss + 16 * hh;
+        const int ln = lane_now();
+        const uint8_t* qp = qbh + (int64_t)(row0 + (ln & 31)) * a.mq.ss + 16 * (ln >> 5);
 #pragma unroll
         for (int m = 0; m < QM; ++m) qop[m] = *(const v4i*)(qp + 32 * m);
       }
@@ -327,10 +343,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
         }
       };
 
+      // prologue: only the Q rows and block 0 are waited for before the first barrier; block 1
+      // streams in under the first two phases, each wave waiting for its share at the end of
+      // its S_pro (K(1) is first read in M_0, V(1) in S_0)
       stage(0);
-      stage(1);
       wait_dma();
       lds_barrier();
+      stage(1);
       if (grp == 1) lds_barrier();
 
       if (live(0)) qk(0);
@@ -340,6 +359,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
         probs();
         preload(0);
       }
+      wait_dma();
       lds_barrier();
 
       for (int i = 0; i < nb; ++i) {
@@ -349,7 +369,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
         if (live_i) stream(i);
         // after this phase's last operand read: K(i+2) by group 0 into the slot of K(i),
         // V(i+2) by group 1 into the slot of V(i-1); waited for at the end of S_i
-        if (i + 2 < nb) stage(i + 2);
+        if (i + 2 < nb) stage_loop(i + 2);
         lds_barrier();
         // -------------------------------------------------------------- S_i
         __builtin_amdgcn_s_setprio(0);
@@ -382,7 +402,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
         }
       {
         uint8_t* orow = (uint8_t*)a.out + b * a.mo.sb + h * a.mo.sh + (int64_t)row0 * a.mo.ss;
-        const int sr = lane >> 4, sc = 16 * (lane & 15);
+        const int ln = lane_now();
+        const int sr = ln >> 4, sc = 16 * (ln & 15);
 #pragma unroll
         for (int s4 = 0; s4 < kWaveRows / 4; ++s4) {
           const int r = 4 * s4 + sr;
@@ -391,6 +412,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
       }
       if (a.lse != nullptr && hh == 0) a.lse[(int64_t)(b * H + h) * S + qrow] = kLn2 * (m + __log2f(lt));
       lds_barrier();
+    }
+    // the workgroup's next item, work.step items on
+    if (item + work.step >= work.end) break;
+    j += work.step;
+    while (j >= sch.P) {
+      j -= sch.P;
+      if (++hg == a.G) {
+        hg = 0;
+        ++hk;
+      }
+      if (++h == H) {
+        h = hg = hk = 0;
+        ++b;
+      }
     }
   }
 }

@@ -113,6 +113,41 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 __device__ __forceinline__ void dma16(const void* gsrc, uint8_t* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(gsrc, (lds_void_t*)lds_wave_base, 16, 0, 0);
 }
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_void_t*)p;
+}
+
+// One 64-cell copy round from global memory into LDS (lane L writes cell base + L), in the form
+// the FP8 kernel's hand-ordered matrix phase also uses: a wave-uniform 64-bit base in scalar
+// registers plus each lane's 32-bit offset, with M0 = the round's LDS base (saved and
+// restored).  With a per-lane 64-bit address (the builtin's form) the compiler keeps one
+// address pair per round, spills them, and reloads them with a wait for every load in flight.  Five wait states come first in case the compiler
+// has just written a scalar operand from a vector instruction (a spill reload), and one after
+// the M0 write.
+__device__ __forceinline__ void copy_round(uint64_t gs, uint32_t m, uint32_t off) {
+  int t;
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b32 %[t], m0\n\t"
+      "s_mov_b32 m0, %[m]\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %[o], %[gs]\n\t"
+      "s_mov_b32 m0, %[t]"
+      : [t] "=&s"(t)
+      : [m] "s"(m), [o] "v"(off), [gs] "s"(gs)
+      : "memory");
+}
+
+// The lane index, read afresh at its point of use.  Per-lane address offsets computed from it
+// inside the tile loop then live only there: computed once at the top of the kernel, the
+// compiler keeps them (widened to 64 bits) across the whole kernel, spills them, and reloads them
+// at every work item with a wait for every memory access in flight.
+__device__ __forceinline__ int lane_now() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // s_waitcnt vmcnt(0) (gfx9 encoding: expcnt and lgkmcnt at their maxima), issued as the
 // builtin so the compiler's own wait insertion knows the counter is drained afterwards
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }

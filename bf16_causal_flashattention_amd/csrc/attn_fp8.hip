@@ -118,31 +118,6 @@ __device__ __forceinline__ float max2(float a, float b) {
   return r;
 }
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const lds_void_t*)p;
-}
-
-// One 64-cell copy round from global memory into LDS, in the form the hand-ordered matrix
-// phase uses: a wave-uniform 64-bit base in scalar registers plus each lane's 32-bit offset,
-// with M0 = the round's LDS base (saved and restored).  With a per-lane 64-bit address the
-// compiler keeps one address pair per round, spills them, and reloads them with a wait for
-// every load in flight before each copy.  Five wait states come first in case the compiler
-// has just written a scalar operand from a vector instruction (a spill reload), and one after
-// the M0 write.
-__device__ __forceinline__ void copy_round(uint64_t gs, uint32_t m, uint32_t off) {
-  int t;
-  asm volatile(
-      "s_nop 4\n\t"
-      "s_mov_b32 %[t], m0\n\t"
-      "s_mov_b32 m0, %[m]\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %[o], %[gs]\n\t"
-      "s_mov_b32 m0, %[t]"
-      : [t] "=&s"(t)
-      : [m] "s"(m), [o] "v"(off), [gs] "s"(gs)
-      : "memory");
-}
-
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -222,10 +197,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
   const float cp = a.cp;
   const float cp8 = 8.0f * cp;
 
+  // (b, h, j) of the workgroup's first item; later items follow by scalar increments, so the
+  // loop holds no division (whose reciprocals the compiler would keep in vector registers)
+  int b, h, j;
+  decode_item(work.first, H, sch.P, b, h, j);
+  int hk = h / a.G, hg = h - hk * a.G;  // key/value head of query head h, and h's place in its group
   for (int64_t item = work.first; item < work.end; item += work.step) {
-    int b, h, j;
-    decode_item(item, H, sch.P, b, h, j);
-    const int hk = h / a.G;  // key/value head of query head h
     const uint8_t* qbh = a.q + b * a.mq.sb + h * a.mq.sh;
     const uint8_t* st_head = stage_k ? a.k + b * a.mk.sb + hk * a.mk.sh : a.v + b * a.mv.sb + hk * a.mv.sh;
     // bytes from one 128-key block to the next in the staged tensor
@@ -253,7 +230,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
       // ---------------------------------------------------------------- per-wave state
       v8i qop[KC];
       {
-        const uint8_t* qp = qbh + (int64_t)qrow * a.mq.ss + 32 * hh;
+        const int ln = lane_now();
+        const uint8_t* qp = qbh + (int64_t)(row0 + (ln & 31)) * a.mq.ss + 32 * (ln >> 5);
 #pragma unroll
         for (int c = 0; c < KC; ++c) qop[c] = *(const v8i*)(qp + 64 * c);
       }
@@ -963,7 +941,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
         }
       {
         uint8_t* orow = (uint8_t*)a.out + b * a.mo.sb + h * a.mo.sh + (int64_t)row0 * a.mo.ss;
-        const int sr = lane >> 4, sc = 16 * (lane & 15);
+        const int ln = lane_now();
+        const int sr = ln >> 4, sc = 16 * (ln & 15);
 #pragma unroll
         for (int s4 = 0; s4 < kWaveRows / 4; ++s4) {
           const int r = 4 * s4 + sr;
@@ -973,6 +952,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
       if (a.lse != nullptr && hh == 0)
         a.lse[(int64_t)(b * H + h) * S + qrow] = kLn2 * (m + __log2f(l) - (float)kSigma);
       lds_barrier();
+    }
+    // the workgroup's next item, work.step items on
+    if (item + work.step >= work.end) break;
+    j += work.step;
+    while (j >= sch.P) {
+      j -= sch.P;
+      if (++hg == a.G) {
+        hg = 0;
+        ++hk;
+      }
+      if (++h == H) {
+        h = hg = hk = 0;
+        ++b;
+      }
     }
   }
 }
