@@ -16,6 +16,9 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-ffp-contract=off",                       # fp32 order is part of the oracle contract
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # loop headers on 64-byte boundaries: without it the speed of the attention loops moved by
+    # up to 2% with the placement of unrelated code (the epilogue, say) in the same kernel
+    "-falign-loops=64",
     "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
     "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
 ]

@@ -100,14 +100,6 @@ __device__ __forceinline__ void barrier_reads_in_flight() {
 
 __device__ __forceinline__ v8bf as_bf(v4i x) { return __builtin_bit_cast(v8bf, x); }
 
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
-  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-  bf2 r;
-  r[0] = (__bf16)lo;
-  r[1] = (__bf16)hi;
-  return __builtin_bit_cast(uint32_t, r);
-}
-
 // O staging for the epilogue: a 32-row area per wave with a 272-byte row pitch, so the
 // 16-byte pieces that 16 consecutive rows write at one column fall on distinct banks
 constexpr int kStgPitch = 272;

@@ -212,8 +212,15 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float x) {
   const uint32_t u = __float_as_uint(x);
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return bf16_bits_rne(lo) | (bf16_bits_rne(hi) << 16);
+// two fp32 values to packed bf16 (lo in the low half), rounded to nearest even: the compiler
+// lowers the conversion to one v_cvt_pk_bf16_f32 on gfx950
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  bf2 r;
+  r[0] = (__bf16)lo;
+  r[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, r);
 }
+
 
 }  // namespace cfa

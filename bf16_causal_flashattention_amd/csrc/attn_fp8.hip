@@ -935,8 +935,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
         for (int g = 0; g < 4; ++g) {
           const int d0 = 32 * dt + 8 * g + 4 * hh;
           uint2 w;
-          w.x = pack_bf16x2(oacc[dt][4 * g + 0] * inv, oacc[dt][4 * g + 1] * inv);
-          w.y = pack_bf16x2(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
+          w.x = cvt_pk_bf16(oacc[dt][4 * g + 0] * inv, oacc[dt][4 * g + 1] * inv);
+          w.y = cvt_pk_bf16(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
           *(uint2*)(stg + l32 * kStgPitch + 2 * d0) = w;
         }
       {
