@@ -268,3 +268,33 @@ def _bf16_ex_check(q, k, v, layout):
     print("RESULT", res, flush=True)
     assert res["fp64_rms"] <= TOL_FP64_RMS_BF16, res
     assert res["lse_fp64"] <= 1e-3 + 1e-6 * np.max(np.abs(ex_lse)), res
+
+
+@pytest.mark.parametrize("kind,dqk", [("fp8", 128), ("fp8", 192), ("bf16", 128), ("bf16", 192)])
+@pytest.mark.parametrize("B,H,Hkv,S", [(3, 96, 48, 512), (2, 10, 5, 8192)])
+def test_many_items_per_workgroup(kind, dqk, B, H, Hkv, S):
+    """More tile pairs than workgroups (288 and 320 items for at most 256 workgroups), over
+    several batches and grouped key/value heads: a workgroup then steps through several work
+    items, from one pair of a head to the next (S = 8192, 16 pairs per head) and across heads
+    and batches (S = 512, one pair per head).  A causal row does not depend on which workgroup
+    runs it, so every (b, h) of the launch must equal a launch on that head alone, bit for bit."""
+    _case("many items per workgroup", kind, dqk, B, H, Hkv, S)
+    G = H // Hkv
+    q, k, v = _inputs(B, H, Hkv, S, dqk, seed=B * H + S + dqk)
+    if kind == "fp8":
+        (qg, dq), (kg, dk), (vg, dv) = [(c_, float(d_.item())) for c_, d_ in
+                                        (cfa.quantize_e4m3(torch.from_numpy(x).to(DEV)) for x in (q, k, v))]
+        run = lambda a, b_, c: cfa.attn_fwd_causal_fp8_ex(a, b_, c, dq, dk, dv)
+    else:
+        qg, kg, vg = (cfa.round_bf16(torch.from_numpy(x).to(DEV)) for x in (q, k, v))
+        run = lambda a, b_, c: cfa.attn_fwd_causal_bf16_ex(a, b_, c)
+    out, lse = run(qg, kg, vg)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out.float()).any() and not torch.isnan(lse).any()
+    for b in range(B):
+        for h in range(H):
+            o1, l1 = run(qg[b:b + 1, :, h:h + 1].contiguous(), kg[b:b + 1, :, h // G:h // G + 1].contiguous(),
+                         vg[b:b + 1, :, h // G:h // G + 1].contiguous())
+            assert torch.equal(out[b:b + 1, :, h:h + 1].contiguous().view(torch.int16), o1.view(torch.int16)), (b, h)
+            assert torch.equal(lse[b, h], l1[0, 0]), (b, h)
+    torch.cuda.synchronize()
