@@ -1,11 +1,12 @@
 // Causal attention forward with BF16 operands on gfx950 MFMA (v_mfma_f32_32x32x16_bf16).
 //
 // Follows "ZYFA: Speed and Accuracy of FP8 FlashAttention on AMD CDNA4":
-//   Sec. II-B  base-2 online softmax over 64-key blocks, LSE output;
+//   Sec. II-B  base-2 online softmax over key blocks (128 keys at d_qk = 128, as the paper
+//              prices a BF16 block in Table III; 64 at the MLA shape), LSE output;
 //   Sec. IV-A  8 waves x 32 query rows, S^T = K Q^T so each lane holds one query's
 //              scores, causal pairing, persistent grid, chiplet map, lazy rescaling
 //              with tau = 4 at d_qk = 128 and 8 at the MLA shape d_qk = 192;
-//   Sec. VI-A  dead-block skip: in the diagonal blocks a wave skips the 64-key blocks
+//   Sec. VI-A  dead-block skip: in the diagonal blocks a wave skips the key blocks
 //              that the causal mask hides from all its rows (loads and barriers still run);
 //   Sec. IV-D  the 8-wave ping-pong of the BF16 d = 128 kernel: the two waves of a SIMD
 //              alternate between issuing the block's matrix products and computing the
@@ -21,11 +22,14 @@
 // before), so the matrix phase starts with its operands in registers.  On a wave's last
 // live block the QK part still runs, on the other K slot (in-bounds LDS, scores unused),
 // which keeps one shape of the stream.  S_i takes the next block's maximum, the lazy
-// decision (with the rare rescale of O and l) and forms P(i+1).  K and V blocks move by DMA issued at the end
-// of M_i, after the phase's last operand read: group 0 copies K(i+2) into the slot of
-// K(i) (two K slots), group 1 copies V(i+2) into the slot of V(i-1) (three V slots); each
-// wave waits for its copies at the end of S_i.  Every target slot was last read in an
-// earlier phase and every copy completes at least one phase before its first read.
+// decision (with the rare rescale of O and l) and forms P(i+1).  K and V blocks move by DMA:
+// group 0 copies K(i+2) into the slot of K(i) (two K slots) at the end of M_i, after the
+// phase's last operand read.  With three V slots (d_qk = 192) group 1 copies V(i+2) into the
+// slot of V(i-1) at the end of its M_i; with two (d_qk = 128, whose 128-key slots leave no room
+// for a third) it copies V(i+2) into the slot of V(i) at the start of its S_i, once the barrier
+// has closed both groups' reads of V(i).  Each wave waits for its copies at the end of S_i.
+// Every target slot was last read before the copy's issuing barrier and every copy
+// completes at least one phase before its first read.
 // The epilogue stores O as whole rows through a per-wave LDS staging area, as in the FP8
 // kernel.
 //
@@ -46,7 +50,7 @@ template <int DQK>
 constexpr float kTauBf16 = DQK == 128 ? 4.0f : 8.0f;
 constexpr float kLn2 = 0.69314718055994530942f;
 
-// LDS: two K slots then three V slots, each a run of 16-byte cells filled by DMA
+// LDS: two K slots then two or three V slots, each a run of 16-byte cells filled by DMA
 // (global_load_lds: lane L of a wave writes cell base + L); pad cells receive a copy of a
 // data cell of the same row (no per-lane masking) and are never read.
 //   K slot: row 32*(key/32) + key_perm_bf16(key%32) holds key `key` (key_perm_bf16 is an
@@ -59,9 +63,14 @@ constexpr float kLn2 = 0.69314718055994530942f;
 //           half read neighbouring 32-byte pieces of the same rows; with a 320-byte stride the
 //           8 pieces of 32 lanes fall on distinct banks (a 288-byte stride made them collide,
 //           measured as 5.4e8 bank-conflict cycles per call at B1 H32 S32768, now 3e6).
-constexpr int kBlk = 64;  // keys per block (max update, ping-pong phase and LDS slot)
+// keys per block (max update, ping-pong phase and LDS slot): 128 at d_qk = 128, where two K and
+// two V slots fit LDS; 64 at d_qk = 192, whose 400-byte K rows leave room for three V slots
+template <int DQK>
+constexpr int kBlkOf = DQK == 128 ? 128 : 64;
 template <int DQK>
 struct Bf16Lds {
+  static constexpr int kBlk = kBlkOf<DQK>;
+  static constexpr int kVSlots = DQK == 128 ? 2 : 3;
   static constexpr int kKCols = DQK / 8;  // 16-byte data cells per K row
   static constexpr int kKSpr = kKCols + 1;
   static constexpr int kKStride = 16 * kKSpr;
@@ -72,7 +81,7 @@ struct Bf16Lds {
   static constexpr int kVCells = kBlk * kVSpr;
   static constexpr int kVSlot = 16 * kVCells;
   static constexpr int kVBase = 2 * kKSlot;
-  static constexpr int kLdsBytes = 2 * kKSlot + 3 * kVSlot;
+  static constexpr int kLdsBytes = 2 * kKSlot + kVSlots * kVSlot;
   static constexpr int kRounds = ((kKCells > kVCells ? kKCells : kVCells) + 255) / 256;
 };
 
@@ -100,6 +109,29 @@ __device__ __forceinline__ void barrier_reads_in_flight() {
 
 __device__ __forceinline__ v8bf as_bf(v4i x) { return __builtin_bit_cast(v8bf, x); }
 
+// maximum of N floats that are never NaN, as a tree of three-input maxima
+template <int N>
+__device__ __forceinline__ float max_tree(const float* x) {
+  if constexpr (N == 1) {
+    return x[0];
+  } else if constexpr (N == 2) {
+    return max2(x[0], x[1]);
+  } else {
+    constexpr int M = (N + 2) / 3;
+    float y[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      if (3 * i + 2 < N)
+        y[i] = fmax3(x[3 * i], x[3 * i + 1], x[3 * i + 2]);
+      else if (3 * i + 1 < N)
+        y[i] = max2(x[3 * i], x[3 * i + 1]);
+      else
+        y[i] = x[3 * i];
+    }
+    return max_tree<M>(y);
+  }
+}
+
 // O staging for the epilogue: a 32-row area per wave with a 272-byte row pitch, so the
 // 16-byte pieces that 16 consecutive rows write at one column fall on distinct banks
 constexpr int kStgPitch = 272;
@@ -112,6 +144,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
   constexpr int kKStride = L::kKStride, kKCells = L::kKCells, kKSlot = L::kKSlot, kKSpr = L::kKSpr;
   constexpr int kVStride = L::kVStride, kVCells = L::kVCells, kVSlot = L::kVSlot, kVSpr = L::kVSpr;
   constexpr int kVBase = L::kVBase, kRounds = L::kRounds;
+  constexpr int kBlk = L::kBlk, kVS = L::kVSlots;
+  constexpr int NU = kBlk / 32;  // 32-key sub-tiles of a block (score accumulators)
+  constexpr int NM = kBlk / 16;  // 16-key steps of a block (P operands)
   constexpr int QM = DQK / 16;  // 16-deep k steps of S^T = K Q^T
   constexpr float kTau = kTauBf16<DQK>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[L::kLdsBytes];
@@ -172,7 +207,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
       if (pass == 1 && tile == sch.T - 1 - j) break;
       const int row0 = tile * kTileRows + wave * kWaveRows;
       const int qrow = row0 + l32;
-      const int nb = 4 * tile + 4;  // 64-key blocks
+      const int nb = (tile + 1) * (kTileRows / kBlk);  // key blocks
 
       // DMA of block blk: K into slot blk % 2, V into slot blk % 3.  The prologue copies go
       // through a scalar base (copy_round: no per-lane 64-bit addresses to keep, spill and reload
@@ -182,14 +217,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
       auto stage = [&](int blk) {
         const uint64_t gs = (uint64_t)(uintptr_t)(st_head + (int64_t)(blk * kBlk) * st_rs);  // wave-uniform
         const uint32_t mb = __builtin_amdgcn_readfirstlane(
-            lds_addr(smem) + st_lds + (stage_k ? (blk & 1) * kKSlot : (blk % 3) * kVSlot));
+            lds_addr(smem) + st_lds + (stage_k ? (blk & 1) * kKSlot : (blk % kVS) * kVSlot));
 #pragma unroll
         for (int p = 0; p < kRounds; ++p)
           if (256 * p + 64 * wq < st_cells) copy_round(gs, mb + 4096 * p, st_goff[p]);
       };
       auto stage_loop = [&](int blk) {
         const uint8_t* src = st_head + (int64_t)(blk * kBlk) * st_rs;
-        uint8_t* dst = smem + st_lds + (stage_k ? (blk & 1) * kKSlot : (blk % 3) * kVSlot);
+        uint8_t* dst = smem + st_lds + (stage_k ? (blk & 1) * kKSlot : (blk % kVS) * kVSlot);
 #pragma unroll
         for (int p = 0; p < kRounds; ++p)
           if (256 * p + 64 * wq < st_cells) dma16(src + st_goff[p], dst + 4096 * p);
@@ -205,8 +240,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
       v16f oacc[4];
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) oacc[dt] = zero16;
-      v16f sacc[2];  // scores of the next block (two 32-key sub-tiles)
-      v4i pb[4];     // P^T operand per 16-key step
+      v16f sacc[NU];  // scores of the next block (32-key sub-tiles)
+      v4i pb[NM];     // P^T operand per 16-key step
       float m = 0.f, l = 0.f;
 
       auto live = [&](int blk) { return blk * kBlk <= row0 + kWaveRows - 1; };
@@ -214,15 +249,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
       // independent, and each MFMA's operand is read one MFMA ahead.
       auto qk = [&](int blk) {
         const uint8_t* sk = smem + (blk & 1) * kKSlot + k_rd;
-        auto kread = [&](int t) { return *(const v4i*)(sk + 32 * (t & 1) * kKStride + 32 * (t >> 1)); };
-        constexpr int D = 3;       // operand reads in flight ahead of the MFMAs
-        constexpr int N = 2 * QM;  // MFMAs
+        auto kread = [&](int t) { return *(const v4i*)(sk + 32 * (t % NU) * kKStride + 32 * (t / NU)); };
+        constexpr int D = 3;        // operand reads in flight ahead of the MFMAs
+        constexpr int N = NU * QM;  // MFMAs
         v4i kop[D + 1];
 #pragma unroll
         for (int t = 0; t < D; ++t) kop[t] = kread(t);
 #pragma unroll
         for (int t = 0; t < N; ++t) {
-          const int u = t & 1, mm = t >> 1;
+          const int u = t % NU, mm = t / NU;
           if (t + D < N) kop[(t + D) % (D + 1)] = kread(t + D);
           sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(kop[t % (D + 1)]), as_bf(qop[mm]),
                                                             mm == 0 ? zero16 : sacc[u], 0, 0, 0);
@@ -241,20 +276,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
         const int key0 = blk * kBlk;
         if (key0 + kBlk - 1 > row0) {
 #pragma unroll
-          for (int u = 0; u < 2; ++u)
+          for (int u = 0; u < NU; ++u)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
               if (key0 + 32 * u + 16 * (r >> 3) + 8 * hh + (r & 7) > qrow) sacc[u][r] = -INFINITY;
         }
-        // v_max3 tree over the 32 scores of the lane
-        float x[11];
+        // v_max3 tree over the lane's scores of the block
+        float x[NU * 16];
 #pragma unroll
-        for (int k = 0; k < 5; ++k) x[k] = fmax3(sacc[0][3 * k], sacc[0][3 * k + 1], sacc[0][3 * k + 2]);
-        x[5] = fmax3(sacc[0][15], sacc[1][0], sacc[1][1]);
+        for (int u = 0; u < NU; ++u)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) x[6 + k] = fmax3(sacc[1][2 + 3 * k], sacc[1][3 + 3 * k], sacc[1][4 + 3 * k]);
-        x[10] = max2(sacc[1][14], sacc[1][15]);
-        const float y = fmax3(fmax3(x[0], x[1], x[2]), fmax3(x[3], x[4], x[5]), fmax3(fmax3(x[6], x[7], x[8]), x[9], x[10]));
+          for (int r = 0; r < 16; ++r) x[16 * u + r] = sacc[u][r];
+        const float y = max_tree<NU * 16>(x);
         const uint32_t yu = __float_as_uint(y);
         const auto sw = __builtin_amdgcn_permlane32_swap(yu, yu, false, false);
         const float tmax = max2(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * cp;
@@ -274,7 +307,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
       auto probs = [&]() {
         const float nm = -m;
 #pragma unroll
-        for (int mm = 0; mm < 4; ++mm) {
+        for (int mm = 0; mm < NM; ++mm) {
           const int u = mm >> 1, r0 = 8 * (mm & 1);
           float p[8];
 #pragma unroll
@@ -288,37 +321,37 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
       // the 2 QM QK MFMAs of block blk+1.  Operand t is read kDist MFMAs ahead of its MFMA
       // through the ring opb; the first kDist (V operands) are read by preload().
       constexpr int kDist = 3;
-      constexpr int NQ = 2 * QM;
+      constexpr int NQ = NU * QM;
       v4i opb[kDist + 1];
       // lane: V^T operand d = 32dt + l32 over keys 16mm + 8hh + 0..7 (two transpose reads);
       // K operand as in qk()
       auto opread = [&](int blk, int t) -> v4i {
-        if (t < 16) {
-          const uint8_t* sv = smem + (blk % 3) * kVSlot + v_tr;
+        if (t < 4 * NM) {
+          const uint8_t* sv = smem + (blk % kVS) * kVSlot + v_tr;
           const int dt = t & 3, mm = t >> 2;
           const v2i r0 = lds_tr16(sv + (16 * mm) * kVStride + 64 * dt);
           const v2i r1 = lds_tr16(sv + (16 * mm + 4) * kVStride + 64 * dt);
           return (v4i){r0[0], r0[1], r1[0], r1[1]};
         }
-        const int tq = t - 16;
+        const int tq = t - 4 * NM;
         const uint8_t* sk = smem + ((blk + 1) & 1) * kKSlot + k_rd;
-        return *(const v4i*)(sk + 32 * (tq & 1) * kKStride + 32 * (tq >> 1));
+        return *(const v4i*)(sk + 32 * (tq % NU) * kKStride + 32 * (tq / NU));
       };
       auto preload = [&](int blk) {
 #pragma unroll
         for (int t = 0; t < kDist; ++t) opb[t] = opread(blk, t);
       };
       auto stream = [&](int blk) {
-        constexpr int N = 16 + NQ;
+        constexpr int N = 4 * NM + NQ;
 #pragma unroll
         for (int t = 0; t < N; ++t) {
           if (t + kDist < N) opb[(t + kDist) % (kDist + 1)] = opread(blk, t + kDist);
           const v4i op = opb[t % (kDist + 1)];
-          if (t < 16) {
+          if (t < 4 * NM) {
             const int dt = t & 3, mm = t >> 2;
             oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(op), as_bf(pb[mm]), oacc[dt], 0, 0, 0);
           } else {
-            const int tq = t - 16, u = tq & 1, mm = tq >> 1;
+            const int tq = t - 4 * NM, u = tq % NU, mm = tq / NU;
             sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(op), as_bf(qop[mm]), mm == 0 ? zero16 : sacc[u],
                                                               0, 0, 0);
           }
@@ -327,7 +360,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
 #pragma unroll
         for (int t = 0; t < N; ++t) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          const int nr = t + kDist < N ? (t + kDist < 16 ? 2 : 1) : 0;
+          const int nr = t + kDist < N ? (t + kDist < 4 * NM ? 2 : 1) : 0;
           if (nr == 2)
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
           else if (nr == 1)
@@ -359,19 +392,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
         __builtin_amdgcn_s_setprio(1);
         const bool live_i = live(i), live_n = (i + 1 < nb) && live(i + 1);
         if (live_i) stream(i);
-        // after this phase's last operand read: K(i+2) by group 0 into the slot of K(i),
-        // V(i+2) by group 1 into the slot of V(i-1); waited for at the end of S_i
-        if (i + 2 < nb) stage_loop(i + 2);
+        // after this phase's last operand read: K(i+2) by group 0 into the slot of K(i), and with
+        // three V slots V(i+2) by group 1 into the slot of V(i-1); waited for at the end of S_i
+        if (i + 2 < nb && (stage_k || kVS == 3)) stage_loop(i + 2);
         lds_barrier();
         // -------------------------------------------------------------- S_i
         __builtin_amdgcn_s_setprio(0);
+        // with two V slots, V(i+2) goes into the slot of V(i), which this group read in M_i and
+        // the other group a phase earlier: free only after the barrier just passed
+        if (kVS == 2 && !stage_k && i + 2 < nb) stage_loop(i + 2);
         if (live_n) {
           max_step(i + 1, false);
           probs();
         }
         if (i + 2 < nb) wait_dma();
         // V(i+1): its copy was waited for at least one phase ago, and its slot is next written
-        // in M_{i+2} (by V(i+4)), so the reads may complete after the barrier
+        // at the start of the other group's S_{i+1} (two V slots) or in M_{i+2} (three), after
+        // this wave's M_{i+1} has used the reads, so they may complete after the barrier
         if (live_n) preload(i + 1);
         barrier_reads_in_flight();
       }
