@@ -209,11 +209,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
       const int qrow = row0 + l32;
       const int nb = (tile + 1) * (kTileRows / kBlk);  // key blocks
 
-      // DMA of block blk: K into slot blk % 2, V into slot blk % 3.  The prologue copies go
-      // through a scalar base (copy_round: no per-lane 64-bit addresses to keep, spill and reload
-      // at every tile start); the loop's copies, one block per 64 keys, keep the builtin, whose
-      // per-lane address costs less there than the asm round's fixed wait states and M0 handling
-      // (measured 0.5-1% at 16K-32K)
+      // DMA of block blk: K into slot blk % 2, V into slot blk % kVS.  stage() goes through a
+      // scalar base (copy_round: no per-lane 64-bit addresses, which the compiler would keep,
+      // spill and reload at every tile start, and no vector instructions to form them): the
+      // prologue uses it, and so does the loop at d_qk = 128, where group 1 issues its V copies
+      // inside the softmax phase and the address arithmetic of the builtin competed with the
+      // softmax (4.5% at 16K-32K).  With 64-key blocks (d_qk = 192) the loop keeps the builtin,
+      // whose per-lane address cost less there than the asm round's wait states and M0 handling.
       auto stage = [&](int blk) {
         const uint64_t gs = (uint64_t)(uintptr_t)(st_head + (int64_t)(blk * kBlk) * st_rs);  // wave-uniform
         const uint32_t mb = __builtin_amdgcn_readfirstlane(
@@ -394,13 +396,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
         if (live_i) stream(i);
         // after this phase's last operand read: K(i+2) by group 0 into the slot of K(i), and with
         // three V slots V(i+2) by group 1 into the slot of V(i-1); waited for at the end of S_i
-        if (i + 2 < nb && (stage_k || kVS == 3)) stage_loop(i + 2);
+        if (i + 2 < nb && (stage_k || kVS == 3)) {
+          if constexpr (kVS == 2)
+            stage(i + 2);
+          else
+            stage_loop(i + 2);
+        }
         lds_barrier();
         // -------------------------------------------------------------- S_i
         __builtin_amdgcn_s_setprio(0);
         // with two V slots, V(i+2) goes into the slot of V(i), which this group read in M_i and
         // the other group a phase earlier: free only after the barrier just passed
-        if (kVS == 2 && !stage_k && i + 2 < nb) stage_loop(i + 2);
+        if (kVS == 2 && !stage_k && i + 2 < nb) stage(i + 2);  // through the scalar base
         if (live_n) {
           max_step(i + 1, false);
           probs();
