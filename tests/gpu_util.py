@@ -23,8 +23,10 @@ LSE_EMU_NATS = 0.02
 # FP8 MFMA score error bound on gfx950: |s_gpu - s_exact| <= 2^-10 times the largest
 # |q_d k_d| product of each 64-wide chunk, summed over the chunks, plus two fp32 roundings
 # of the sum.  The MFMA does not round its 64-term sums correctly (about 2^-11 of the
-# largest product was measured); test_gpu_scores.py checks this bound on every score of
-# its cases.
+# largest product is measured).  check_fp8_on_gpu_scores checks the bound on every score the
+# kernel forms (test_gpu_parity.py::test_decisions_on_gpu_scores, including full-range e4m3
+# inputs, and the prefix check of the activation-like full-size test) and reports the largest
+# error over bound, 0.5-0.6 in the runs so far.
 MFMA_ERR_PER_CHUNK = 2.0 ** -10
 # exact P: the GPU's 2^x (v_exp_f32) is within about an fp32 ulp; a code may round the
 # other way when 2^x lies this close (relative) to an e4m3 rounding boundary
