@@ -11,28 +11,27 @@
 //   Sec. IV-B3         row sum of the rounded probabilities on the matrix unit;
 //   Sec. IV-C, Fig. 6  two-wave ping-pong: the two waves of a SIMD alternate between an
 //                      MFMA phase and a softmax phase, with a workgroup barrier per phase.
-//                      At d_qk = 128 with key-major V the matrix phase is one block of
-//                      hand-ordered instructions and, as the paper's MFMA wave does, takes
-//                      the block maxima of the next block between its PV MFMAs; elsewhere
-//                      the softmax phase takes them.
+//                      The matrix phase is one block of hand-ordered instructions and, as
+//                      the paper's MFMA wave does, takes the block maxima of the next block
+//                      between its PV MFMAs.
 //
 // Schedule per 256-row tile with nb 128-key blocks.  Group g = wave / 4 (one wave of
 // each group per SIMD).  Group 1 runs one phase behind group 0:
 //   group 0:  M_pro S_pro M_0 S_0 M_1 S_1 ... M_{nb-1} S_{nb-1} idle
 //   group 1:  idle  M_pro S_pro M_0 S_0 ... M_{nb-1} S_{nb-1}
 // M_i (matrix phase): row sums of P(i); S(i+1) = K(i+1) Q^T; O += V(i)^T P(i); l update;
-//      at d_qk = 128 with key-major V also the block maxima of S(i+1) (blocks below the
-//      diagonal; the softmax phase redoes them with the causal mask on the diagonal).
-// S_i (softmax phase): block maxima of S(i+1) where the matrix phase did not take them,
-//      lazy decision (and the rare rescale of O and l), o(i+1), P(i+1).
+//      the block maxima of S(i+1) (the softmax phase redoes them with the causal mask on the
+//      two diagonal blocks of a tile).
+// S_i (softmax phase): the masked block maxima on the diagonal, lazy decision (and the rare
+//      rescale of O and l), o(i+1), P(i+1).
 // Staging by DMA (global_load_lds, no registers): at the end of M_i, after its last
 // operand read, group 0 copies K(i+2) into the slot of K(i) (two K slots) and group 1
 // copies V(i+2) into the slot of V(i-1) (three V slots); each wave waits for its copies at
 // the end of S_i.  Every target slot was last read in an earlier phase, every copy
 // completes at least one phase before its first read, and the softmax phase reads no
-// LDS, so nothing waits on a copy early.  In the hand-ordered matrix phase every step
-// copies: in a tile's last two steps, which have no block i+2, the wave copies the tile's
-// last block again into the slot the schedule frees.
+// LDS, so nothing waits on a copy early.  Every step copies: in a tile's last two steps,
+// which have no block i+2, the wave copies the tile's last block again into the slot the
+// schedule frees.
 // Epilogue: after the tile's last barrier no wave reads K or V, so each wave writes its
 // 32 rows of bf16 O into a staging area of its own at the start of LDS and stores them
 // as whole 256-byte rows; a barrier keeps the next tile's copies out until every wave
@@ -155,6 +154,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
   // a 64-key block n are keys 64n + 16 hh + {0, 8, 32, 40} + 0..7 (Sec. IV-A layout of P).
   // source lane s of a 16-lane group reads key 16hh + s/2 (+ the piece and block offsets), in
   // row v_row_of_key(16hh + s/2), bytes 16 ((lane/16) % 2) + 8 (s%2) of column group dt
+  // channel-major V: lane l32 of lane half hh reads channel row 32 dt + l32 at byte 32 hh of the
+  // 64-key scale block (two 16-byte reads per operand)
+  const int vt_rd = L::kVBase + l32 * (16 * L::kVtSpr) + 32 * hh;
   const int v_tr = L::kVBase + v_row_offset(v_row_of_key(16 * hh + ((lane & 15) >> 1))) + 16 * ((lane >> 4) & 1) +
                    8 * (lane & 1);
 
@@ -191,7 +193,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
   // iff (L/16)%2 == ((L%16)/4)%2, so every lane receives the sum of its own query.
   const int sel_on = (((lane >> 4) & 1) == (((lane & 15) >> 2) & 1));
   const int selw = sel_on ? 0x38383838 : 0;
-  const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
   const v16f zero16 = {};
 
   const float cp = a.cp;
@@ -245,14 +246,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
 
       auto live = [&](int blk) { return blk * kBlockKeys <= row0 + kWaveRows - 1; };
 
-      // row sums of the codes of the current block (Sec. IV-B3); register operands only, so
-      // these MFMAs start the matrix phase while the first K operand reads are in flight
-      auto rowsum = [&]() {
-        const v8i sel = {selw, selw, selw, selw, selw, selw, selw, selw};
-        const v4f bs0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, pb[0], zero4, 0, 0, 0, 127, 0, 127);
-        const v4f bs1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, pb[1], zero4, 0, 0, 0, 127, 0, 127);
-        return (v2f){bs0[0], bs1[0]};
-      };
       // S^T(blk) = K(blk) Q^T into sacc.  Chunk-outer order keeps consecutive MFMAs
       // independent; the operand of the next MFMA is read before the current one issues.
       auto qk = [&](int blk) {
@@ -280,49 +273,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
       };
-      // O^T += V^T P^T with the 2^-o operand scale; V^T by transpose reads (4 per MFMA), or
-      // for key-contiguous V one 32-byte read per MFMA
-      auto pv = [&](int blk) {
-        const uint8_t* sv = smem + (blk % 3) * L::kVSlot + v_tr;
-        const uint8_t* svt = smem + L::kVBase + (blk % 3) * L::kVSlot + l32 * (16 * L::kVtSpr) + 32 * hh;
-        auto vread = [&](int t) {
-          const int n = t / 4, dt = t % 4;
-          if constexpr (VT) return *(const v8i*)(svt + 32 * dt * (16 * L::kVtSpr) + 64 * n);
-          const uint8_t* p = sv + L::kVHalf * n + 32 * dt;
-          const v2i r0 = lds_tr8(p);
-          const v2i r1 = lds_tr8(p + L::kVPc8);
-          const v2i r2 = lds_tr8(p + L::kVPc32);
-          const v2i r3 = lds_tr8(p + L::kVPc40);
-          return (v8i){r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
-        };
-        v8i vop[2];
-        vop[0] = vread(0);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int n = t / 4, dt = t % 4;
-          if (t + 1 < 8) vop[(t + 1) & 1] = vread(t + 1);
-          oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[t & 1], pb[n], oacc[dt], 0, 0, 0, 127, 0,
-                                                                      127 - o_cur[n]);
-        }
-        if constexpr (DQK == 128) {
-          constexpr int R = VT ? 2 : 4;  // LDS read instructions per operand
-          __builtin_amdgcn_sched_group_barrier(0x100, 2 * R, 1);
-#pragma unroll
-          for (int t = 0; t < 7; ++t) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-            __builtin_amdgcn_sched_group_barrier(0x100, R, 1);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        }
-      };
-      // The matrix phase at d_qk = 128 with key-major V, as one block of hand-ordered
-      // instructions that every step of every wave runs: the row sums of P(i), S^T(i+1) = K Q^T
-      // (8 MFMAs), O^T += V^T(i) P^T(i) (8 MFMAs), and between the PV MFMAs the maxima of the two
+      // The matrix phase, as one block of hand-ordered instructions that every step of every
+      // wave runs: the row sums of P(i), S^T(i+1) = K Q^T (8 MFMAs at d_qk = 128, 12 at 192),
+      // O^T += V^T(i) P^T(i) (8 MFMAs), and between the PV MFMAs the maxima of the two
       // 64-key blocks of S(i+1) (the paper's MFMA wave computes them too, Sec. IV-C; the softmax
       // phase then only takes the lazy decision, o and the codes), then the wave's copies of
       // block i+2.  The first K operand read goes out before the row-sum MFMAs, each later
       // operand read two MFMAs ahead of its MFMA, the first two V^T operands during the last two
-      // QK^T MFMAs; every read is waited for inside the block.  K and V^T operands pass through
+      // QK^T MFMAs; every read is waited for inside the block.  A V^T operand is four
+      // transpose reads from key-major V, or two 16-byte reads from channel-major V (the
+      // assembler's .if on the vt operand picks one).  K and V^T operands pass through
       // two fixed 8-register groups (v240-v255; the second carries the 0/1 row-sum selector
       // first), and the scores sit in v176-v239 so that the maxima can name them.  Copies go
       // through a scalar base and the per-lane 32-bit offsets, with M0 saved and restored.
@@ -334,7 +294,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
       float bm[2];
       auto mphase_asm = [&](int i) -> v2f {
         const uint32_t kb = lds_addr(smem) + ((i + 1) & 1) * L::kKSlot + k_rd;
-        const uint32_t vb = lds_addr(smem) + (i % 3) * L::kVSlot + v_tr;
+        const uint32_t vb = lds_addr(smem) + (i % 3) * L::kVSlot + (VT ? vt_rd : v_tr);
         const int sc0 = 127 - o_cur[0], sc1 = 127 - o_cur[1], one = 127;
         // in a tile's last two steps there is no block i+2: the wave then copies the tile's last
         // block again into the slot the schedule frees (no wave reads it before it is written
@@ -398,83 +358,155 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
             "s_waitcnt lgkmcnt(2)\n\t"
             "v_mfma_scale_f32_32x32x64_f8f6f4 v[208:223], v[240:247], %[q1], v[208:223], %[one], %[one] op_sel_hi:[0,0,0]\n\t"
             // the first two V^T operands of PV(i), four transpose reads each
+            ".if %[vt]\n\t"
+            "ds_read_b128 v[240:243], %[vb]\n\t"
+            "ds_read_b128 v[244:247], %[vb] offset:16\n\t"
+            ".else\n\t"
             "ds_read_b64_tr_b8 v[240:241], %[vb]\n\t"
             "ds_read_b64_tr_b8 v[242:243], %[vb] offset:256\n\t"
             "ds_read_b64_tr_b8 v[244:245], %[vb] offset:4224\n\t"
             "ds_read_b64_tr_b8 v[246:247], %[vb] offset:4480\n\t"
+            ".endif\n\t"
+            ".if %[vt]\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            ".else\n\t"
             "s_waitcnt lgkmcnt(4)\n\t"
+            ".endif\n\t"
             "v_mfma_scale_f32_32x32x64_f8f6f4 v[224:239], v[248:255], %[q1], v[224:239], %[one], %[one] op_sel_hi:[0,0,0]\n\t"
+            ".if %[vt]\n\t"
+            "ds_read_b128 v[248:251], %[vb] offset:4608\n\t"
+            "ds_read_b128 v[252:255], %[vb] offset:4624\n\t"
+            ".else\n\t"
             "ds_read_b64_tr_b8 v[248:249], %[vb] offset:32\n\t"
             "ds_read_b64_tr_b8 v[250:251], %[vb] offset:288\n\t"
             "ds_read_b64_tr_b8 v[252:253], %[vb] offset:4256\n\t"
             "ds_read_b64_tr_b8 v[254:255], %[vb] offset:4512\n\t"
+            ".endif\n\t"
+            ".if %[vt]\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            ".else\n\t"
             "s_waitcnt lgkmcnt(4)\n\t"
+            ".endif\n\t"
             // O^T += V^T(i) P^T(i) with the 2^-o scale of each 64-key block; between these MFMAs the maxima
             // of the two 64-key blocks of S(i+1), each a v_max3 chain over a lane's 32 scores of the block
             // (the scores were written five or more MFMAs earlier)
             "v_mfma_scale_f32_32x32x64_f8f6f4 %[o0], v[240:247], %[p0], %[o0], %[one], %[c0] op_sel_hi:[0,0,0]\n\t"
+            ".if %[vt]\n\t"
+            "ds_read_b128 v[240:243], %[vb] offset:9216\n\t"
+            "ds_read_b128 v[244:247], %[vb] offset:9232\n\t"
+            ".else\n\t"
             "ds_read_b64_tr_b8 v[240:241], %[vb] offset:64\n\t"
             "ds_read_b64_tr_b8 v[242:243], %[vb] offset:320\n\t"
             "ds_read_b64_tr_b8 v[244:245], %[vb] offset:4288\n\t"
             "ds_read_b64_tr_b8 v[246:247], %[vb] offset:4544\n\t"
+            ".endif\n\t"
+            ".if %[vt]\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            ".else\n\t"
             "s_waitcnt lgkmcnt(4)\n\t"
+            ".endif\n\t"
             "v_mfma_scale_f32_32x32x64_f8f6f4 %[o1], v[248:255], %[p0], %[o1], %[one], %[c0] op_sel_hi:[0,0,0]\n\t"
+            ".if %[vt]\n\t"
+            "ds_read_b128 v[248:251], %[vb] offset:13824\n\t"
+            "ds_read_b128 v[252:255], %[vb] offset:13840\n\t"
+            ".else\n\t"
             "ds_read_b64_tr_b8 v[248:249], %[vb] offset:96\n\t"
             "ds_read_b64_tr_b8 v[250:251], %[vb] offset:352\n\t"
             "ds_read_b64_tr_b8 v[252:253], %[vb] offset:4320\n\t"
             "ds_read_b64_tr_b8 v[254:255], %[vb] offset:4576\n\t"
+            ".endif\n\t"
             "v_max3_f32 %[t0], v176, v177, v178\n\t"
             "v_max3_f32 %[t0], %[t0], v179, v180\n\t"
             "v_max3_f32 %[t0], %[t0], v181, v182\n\t"
             "v_max3_f32 %[t0], %[t0], v183, v184\n\t"
             "v_max3_f32 %[t0], %[t0], v185, v186\n\t"
             "v_max3_f32 %[t0], %[t0], v187, v188\n\t"
+            ".if %[vt]\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            ".else\n\t"
             "s_waitcnt lgkmcnt(4)\n\t"
+            ".endif\n\t"
             "v_mfma_scale_f32_32x32x64_f8f6f4 %[o2], v[240:247], %[p0], %[o2], %[one], %[c0] op_sel_hi:[0,0,0]\n\t"
+            ".if %[vt]\n\t"
+            "ds_read_b128 v[240:243], %[vb] offset:64\n\t"
+            "ds_read_b128 v[244:247], %[vb] offset:80\n\t"
+            ".else\n\t"
             "ds_read_b64_tr_b8 v[240:241], %[vb] offset:8448\n\t"
             "ds_read_b64_tr_b8 v[242:243], %[vb] offset:8704\n\t"
             "ds_read_b64_tr_b8 v[244:245], %[vb] offset:12672\n\t"
             "ds_read_b64_tr_b8 v[246:247], %[vb] offset:12928\n\t"
+            ".endif\n\t"
             "v_max3_f32 %[t0], %[t0], v189, v190\n\t"
             "v_max3_f32 %[t0], %[t0], v191, v192\n\t"
             "v_max3_f32 %[t0], %[t0], v193, v194\n\t"
             "v_max3_f32 %[t0], %[t0], v195, v196\n\t"
             "v_max3_f32 %[t0], %[t0], v197, v198\n\t"
+            ".if %[vt]\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            ".else\n\t"
             "s_waitcnt lgkmcnt(4)\n\t"
+            ".endif\n\t"
             "v_mfma_scale_f32_32x32x64_f8f6f4 %[o3], v[248:255], %[p0], %[o3], %[one], %[c0] op_sel_hi:[0,0,0]\n\t"
+            ".if %[vt]\n\t"
+            "ds_read_b128 v[248:251], %[vb] offset:4672\n\t"
+            "ds_read_b128 v[252:255], %[vb] offset:4688\n\t"
+            ".else\n\t"
             "ds_read_b64_tr_b8 v[248:249], %[vb] offset:8480\n\t"
             "ds_read_b64_tr_b8 v[250:251], %[vb] offset:8736\n\t"
             "ds_read_b64_tr_b8 v[252:253], %[vb] offset:12704\n\t"
             "ds_read_b64_tr_b8 v[254:255], %[vb] offset:12960\n\t"
+            ".endif\n\t"
             "v_max3_f32 %[t0], %[t0], v199, v200\n\t"
             "v_max3_f32 %[t0], %[t0], v201, v202\n\t"
             "v_max3_f32 %[t0], %[t0], v203, v204\n\t"
             "v_max3_f32 %[t0], %[t0], v205, v206\n\t"
             "v_max_f32 %[t0], %[t0], v207\n\t"
+            ".if %[vt]\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            ".else\n\t"
             "s_waitcnt lgkmcnt(4)\n\t"
+            ".endif\n\t"
             "v_mfma_scale_f32_32x32x64_f8f6f4 %[o0], v[240:247], %[p1], %[o0], %[one], %[c1] op_sel_hi:[0,0,0]\n\t"
+            ".if %[vt]\n\t"
+            "ds_read_b128 v[240:243], %[vb] offset:9280\n\t"
+            "ds_read_b128 v[244:247], %[vb] offset:9296\n\t"
+            ".else\n\t"
             "ds_read_b64_tr_b8 v[240:241], %[vb] offset:8512\n\t"
             "ds_read_b64_tr_b8 v[242:243], %[vb] offset:8768\n\t"
             "ds_read_b64_tr_b8 v[244:245], %[vb] offset:12736\n\t"
             "ds_read_b64_tr_b8 v[246:247], %[vb] offset:12992\n\t"
+            ".endif\n\t"
             "v_max3_f32 %[t1], v208, v209, v210\n\t"
             "v_max3_f32 %[t1], %[t1], v211, v212\n\t"
             "v_max3_f32 %[t1], %[t1], v213, v214\n\t"
             "v_max3_f32 %[t1], %[t1], v215, v216\n\t"
             "v_max3_f32 %[t1], %[t1], v217, v218\n\t"
             "v_max3_f32 %[t1], %[t1], v219, v220\n\t"
+            ".if %[vt]\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            ".else\n\t"
             "s_waitcnt lgkmcnt(4)\n\t"
+            ".endif\n\t"
             "v_mfma_scale_f32_32x32x64_f8f6f4 %[o1], v[248:255], %[p1], %[o1], %[one], %[c1] op_sel_hi:[0,0,0]\n\t"
+            ".if %[vt]\n\t"
+            "ds_read_b128 v[248:251], %[vb] offset:13888\n\t"
+            "ds_read_b128 v[252:255], %[vb] offset:13904\n\t"
+            ".else\n\t"
             "ds_read_b64_tr_b8 v[248:249], %[vb] offset:8544\n\t"
             "ds_read_b64_tr_b8 v[250:251], %[vb] offset:8800\n\t"
             "ds_read_b64_tr_b8 v[252:253], %[vb] offset:12768\n\t"
             "ds_read_b64_tr_b8 v[254:255], %[vb] offset:13024\n\t"
+            ".endif\n\t"
             "v_max3_f32 %[t1], %[t1], v221, v222\n\t"
             "v_max3_f32 %[t1], %[t1], v223, v224\n\t"
             "v_max3_f32 %[t1], %[t1], v225, v226\n\t"
             "v_max3_f32 %[t1], %[t1], v227, v228\n\t"
             "v_max3_f32 %[t1], %[t1], v229, v230\n\t"
+            ".if %[vt]\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            ".else\n\t"
             "s_waitcnt lgkmcnt(4)\n\t"
+            ".endif\n\t"
             "v_mfma_scale_f32_32x32x64_f8f6f4 %[o2], v[240:247], %[p1], %[o2], %[one], %[c1] op_sel_hi:[0,0,0]\n\t"
             "v_max3_f32 %[t1], %[t1], v231, v232\n\t"
             "v_max3_f32 %[t1], %[t1], v233, v234\n\t"
@@ -523,7 +555,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
             : [kb] "v"(kb), [vb] "v"(vb), [q0] "v"(qop[0]), [q1] "v"(qop[1]), [p0] "v"(pb[0]), [p1] "v"(pb[1]),
               [selw] "v"(selw), [one] "v"(one), [c0] "v"(sc0), [c1] "v"(sc1), [mb] "s"(mb), [gs] "s"(gs),
               [a0] "v"(st_goff[0]), [a1] "v"(st_goff[1]), [a2] "v"(st_goff[2]), [a3] "v"(st_goff[3]),
-              [a4] "v"(st_goff[4]), [nr] "s"(nrounds), [cp] "s"(cp)
+              [a4] "v"(st_goff[4]), [nr] "s"(nrounds), [cp] "s"(cp), [vt] "n"(VT ? 1 : 0)
             : "memory", "scc");
         } else {
         asm volatile(
@@ -591,83 +623,155 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
             "s_waitcnt lgkmcnt(2)\n\t"
             "v_mfma_scale_f32_32x32x64_f8f6f4 v[208:223], v[240:247], %[q2], v[208:223], %[one], %[one] op_sel_hi:[0,0,0]\n\t"
             // the first two V^T operands of PV(i), four transpose reads each
+            ".if %[vt]\n\t"
+            "ds_read_b128 v[240:243], %[vb]\n\t"
+            "ds_read_b128 v[244:247], %[vb] offset:16\n\t"
+            ".else\n\t"
             "ds_read_b64_tr_b8 v[240:241], %[vb]\n\t"
             "ds_read_b64_tr_b8 v[242:243], %[vb] offset:256\n\t"
             "ds_read_b64_tr_b8 v[244:245], %[vb] offset:4224\n\t"
             "ds_read_b64_tr_b8 v[246:247], %[vb] offset:4480\n\t"
+            ".endif\n\t"
+            ".if %[vt]\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            ".else\n\t"
             "s_waitcnt lgkmcnt(4)\n\t"
+            ".endif\n\t"
             "v_mfma_scale_f32_32x32x64_f8f6f4 v[224:239], v[248:255], %[q2], v[224:239], %[one], %[one] op_sel_hi:[0,0,0]\n\t"
+            ".if %[vt]\n\t"
+            "ds_read_b128 v[248:251], %[vb] offset:4608\n\t"
+            "ds_read_b128 v[252:255], %[vb] offset:4624\n\t"
+            ".else\n\t"
             "ds_read_b64_tr_b8 v[248:249], %[vb] offset:32\n\t"
             "ds_read_b64_tr_b8 v[250:251], %[vb] offset:288\n\t"
             "ds_read_b64_tr_b8 v[252:253], %[vb] offset:4256\n\t"
             "ds_read_b64_tr_b8 v[254:255], %[vb] offset:4512\n\t"
+            ".endif\n\t"
+            ".if %[vt]\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            ".else\n\t"
             "s_waitcnt lgkmcnt(4)\n\t"
+            ".endif\n\t"
             // O^T += V^T(i) P^T(i) with the 2^-o scale of each 64-key block; between these MFMAs the maxima
             // of the two 64-key blocks of S(i+1), each a v_max3 chain over a lane's 32 scores of the block
             // (the scores were written five or more MFMAs earlier)
             "v_mfma_scale_f32_32x32x64_f8f6f4 %[o0], v[240:247], %[p0], %[o0], %[one], %[c0] op_sel_hi:[0,0,0]\n\t"
+            ".if %[vt]\n\t"
+            "ds_read_b128 v[240:243], %[vb] offset:9216\n\t"
+            "ds_read_b128 v[244:247], %[vb] offset:9232\n\t"
+            ".else\n\t"
             "ds_read_b64_tr_b8 v[240:241], %[vb] offset:64\n\t"
             "ds_read_b64_tr_b8 v[242:243], %[vb] offset:320\n\t"
             "ds_read_b64_tr_b8 v[244:245], %[vb] offset:4288\n\t"
             "ds_read_b64_tr_b8 v[246:247], %[vb] offset:4544\n\t"
+            ".endif\n\t"
+            ".if %[vt]\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            ".else\n\t"
             "s_waitcnt lgkmcnt(4)\n\t"
+            ".endif\n\t"
             "v_mfma_scale_f32_32x32x64_f8f6f4 %[o1], v[248:255], %[p0], %[o1], %[one], %[c0] op_sel_hi:[0,0,0]\n\t"
+            ".if %[vt]\n\t"
+            "ds_read_b128 v[248:251], %[vb] offset:13824\n\t"
+            "ds_read_b128 v[252:255], %[vb] offset:13840\n\t"
+            ".else\n\t"
             "ds_read_b64_tr_b8 v[248:249], %[vb] offset:96\n\t"
             "ds_read_b64_tr_b8 v[250:251], %[vb] offset:352\n\t"
             "ds_read_b64_tr_b8 v[252:253], %[vb] offset:4320\n\t"
             "ds_read_b64_tr_b8 v[254:255], %[vb] offset:4576\n\t"
+            ".endif\n\t"
             "v_max3_f32 %[t0], v176, v177, v178\n\t"
             "v_max3_f32 %[t0], %[t0], v179, v180\n\t"
             "v_max3_f32 %[t0], %[t0], v181, v182\n\t"
             "v_max3_f32 %[t0], %[t0], v183, v184\n\t"
             "v_max3_f32 %[t0], %[t0], v185, v186\n\t"
             "v_max3_f32 %[t0], %[t0], v187, v188\n\t"
+            ".if %[vt]\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            ".else\n\t"
             "s_waitcnt lgkmcnt(4)\n\t"
+            ".endif\n\t"
             "v_mfma_scale_f32_32x32x64_f8f6f4 %[o2], v[240:247], %[p0], %[o2], %[one], %[c0] op_sel_hi:[0,0,0]\n\t"
+            ".if %[vt]\n\t"
+            "ds_read_b128 v[240:243], %[vb] offset:64\n\t"
+            "ds_read_b128 v[244:247], %[vb] offset:80\n\t"
+            ".else\n\t"
             "ds_read_b64_tr_b8 v[240:241], %[vb] offset:8448\n\t"
             "ds_read_b64_tr_b8 v[242:243], %[vb] offset:8704\n\t"
             "ds_read_b64_tr_b8 v[244:245], %[vb] offset:12672\n\t"
             "ds_read_b64_tr_b8 v[246:247], %[vb] offset:12928\n\t"
+            ".endif\n\t"
             "v_max3_f32 %[t0], %[t0], v189, v190\n\t"
             "v_max3_f32 %[t0], %[t0], v191, v192\n\t"
             "v_max3_f32 %[t0], %[t0], v193, v194\n\t"
             "v_max3_f32 %[t0], %[t0], v195, v196\n\t"
             "v_max3_f32 %[t0], %[t0], v197, v198\n\t"
+            ".if %[vt]\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            ".else\n\t"
             "s_waitcnt lgkmcnt(4)\n\t"
+            ".endif\n\t"
             "v_mfma_scale_f32_32x32x64_f8f6f4 %[o3], v[248:255], %[p0], %[o3], %[one], %[c0] op_sel_hi:[0,0,0]\n\t"
+            ".if %[vt]\n\t"
+            "ds_read_b128 v[248:251], %[vb] offset:4672\n\t"
+            "ds_read_b128 v[252:255], %[vb] offset:4688\n\t"
+            ".else\n\t"
             "ds_read_b64_tr_b8 v[248:249], %[vb] offset:8480\n\t"
             "ds_read_b64_tr_b8 v[250:251], %[vb] offset:8736\n\t"
             "ds_read_b64_tr_b8 v[252:253], %[vb] offset:12704\n\t"
             "ds_read_b64_tr_b8 v[254:255], %[vb] offset:12960\n\t"
+            ".endif\n\t"
             "v_max3_f32 %[t0], %[t0], v199, v200\n\t"
             "v_max3_f32 %[t0], %[t0], v201, v202\n\t"
             "v_max3_f32 %[t0], %[t0], v203, v204\n\t"
             "v_max3_f32 %[t0], %[t0], v205, v206\n\t"
             "v_max_f32 %[t0], %[t0], v207\n\t"
+            ".if %[vt]\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            ".else\n\t"
             "s_waitcnt lgkmcnt(4)\n\t"
+            ".endif\n\t"
             "v_mfma_scale_f32_32x32x64_f8f6f4 %[o0], v[240:247], %[p1], %[o0], %[one], %[c1] op_sel_hi:[0,0,0]\n\t"
+            ".if %[vt]\n\t"
+            "ds_read_b128 v[240:243], %[vb] offset:9280\n\t"
+            "ds_read_b128 v[244:247], %[vb] offset:9296\n\t"
+            ".else\n\t"
             "ds_read_b64_tr_b8 v[240:241], %[vb] offset:8512\n\t"
             "ds_read_b64_tr_b8 v[242:243], %[vb] offset:8768\n\t"
             "ds_read_b64_tr_b8 v[244:245], %[vb] offset:12736\n\t"
             "ds_read_b64_tr_b8 v[246:247], %[vb] offset:12992\n\t"
+            ".endif\n\t"
             "v_max3_f32 %[t1], v208, v209, v210\n\t"
             "v_max3_f32 %[t1], %[t1], v211, v212\n\t"
             "v_max3_f32 %[t1], %[t1], v213, v214\n\t"
             "v_max3_f32 %[t1], %[t1], v215, v216\n\t"
             "v_max3_f32 %[t1], %[t1], v217, v218\n\t"
             "v_max3_f32 %[t1], %[t1], v219, v220\n\t"
+            ".if %[vt]\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            ".else\n\t"
             "s_waitcnt lgkmcnt(4)\n\t"
+            ".endif\n\t"
             "v_mfma_scale_f32_32x32x64_f8f6f4 %[o1], v[248:255], %[p1], %[o1], %[one], %[c1] op_sel_hi:[0,0,0]\n\t"
+            ".if %[vt]\n\t"
+            "ds_read_b128 v[248:251], %[vb] offset:13888\n\t"
+            "ds_read_b128 v[252:255], %[vb] offset:13904\n\t"
+            ".else\n\t"
             "ds_read_b64_tr_b8 v[248:249], %[vb] offset:8544\n\t"
             "ds_read_b64_tr_b8 v[250:251], %[vb] offset:8800\n\t"
             "ds_read_b64_tr_b8 v[252:253], %[vb] offset:12768\n\t"
             "ds_read_b64_tr_b8 v[254:255], %[vb] offset:13024\n\t"
+            ".endif\n\t"
             "v_max3_f32 %[t1], %[t1], v221, v222\n\t"
             "v_max3_f32 %[t1], %[t1], v223, v224\n\t"
             "v_max3_f32 %[t1], %[t1], v225, v226\n\t"
             "v_max3_f32 %[t1], %[t1], v227, v228\n\t"
             "v_max3_f32 %[t1], %[t1], v229, v230\n\t"
+            ".if %[vt]\n\t"
+            "s_waitcnt lgkmcnt(2)\n\t"
+            ".else\n\t"
             "s_waitcnt lgkmcnt(4)\n\t"
+            ".endif\n\t"
             "v_mfma_scale_f32_32x32x64_f8f6f4 %[o2], v[240:247], %[p1], %[o2], %[one], %[c1] op_sel_hi:[0,0,0]\n\t"
             "v_max3_f32 %[t1], %[t1], v231, v232\n\t"
             "v_max3_f32 %[t1], %[t1], v233, v234\n\t"
@@ -729,7 +833,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
               [p0] "v"(pb[0]), [p1] "v"(pb[1]), [selw] "v"(selw), [one] "v"(one), [c0] "v"(sc0), [c1] "v"(sc1),
               [mb] "s"(mb), [gs] "s"(gs), [a0] "v"(st_goff[0]), [a1] "v"(st_goff[1]), [a2] "v"(st_goff[2]),
               [a3] "v"(st_goff[3]), [a4] "v"(st_goff[4]), [a5] "v"(st_goff[NR > 5 ? 5 : 4]),
-              [a6] "v"(st_goff[NR > 6 ? 6 : 4]), [nr] "s"(nrounds), [cp] "s"(cp)
+              [a6] "v"(st_goff[NR > 6 ? 6 : 4]), [nr] "s"(nrounds), [cp] "s"(cp), [vt] "n"(VT ? 1 : 0)
             : "memory", "scc");
         }
         (void)g0;
@@ -875,33 +979,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
       for (int i = 0; i < nb; ++i) {
         // -------------------------------------------------------------- M_i
         __builtin_amdgcn_s_setprio(1);
-        const bool live_i = live(i), live_n = (i + 1 < nb) && live(i + 1);
-        if constexpr (!VT) {
-          // every wave runs the whole stream: a block the causal mask hides from all rows of the
-          // wave has zero codes (set in the softmax phase), so its PV and row sums add 0, and the
-          // scores of a dead or missing next block (its K slot holds an earlier block, in
-          // bounds) are never read
-          v2f bsum;
-          bsum = mphase_asm(i);
+        const bool live_n = (i + 1 < nb) && live(i + 1);
+        // every wave runs the whole stream: a block the causal mask hides from all rows of the
+        // wave has zero codes (set in the softmax phase), so its PV and row sums add 0, and the
+        // scores of a dead or missing next block (its K slot holds an earlier block, in bounds)
+        // are never read
+        {
+          const v2f bsum = mphase_asm(i);
           l = fmaf(bsum[1], __int_as_float((127 - o_cur[1]) << 23), fmaf(bsum[0], __int_as_float((127 - o_cur[0]) << 23), l));
-        } else {
-          v2f bsum = {0.f, 0.f};
-          if (live_i) bsum = rowsum();
-          if (live_n) qk(i + 1);
-          if (live_i) {
-            pv(i);
-            l = fmaf(bsum[1], __int_as_float((127 - o_cur[1]) << 23), fmaf(bsum[0], __int_as_float((127 - o_cur[0]) << 23), l));
-          }
-          // after this phase's last operand read: K(i+2) by group 0 into the slot of K(i),
-          // V(i+2) by group 1 into the slot of V(i-1); waited for at the end of S_i
-          if (i + 2 < nb) stage(i + 2);
         }
         lds_barrier();
         // -------------------------------------------------------------- S_i
         __builtin_amdgcn_s_setprio(0);
         if (live_n) {
           dump_scores(i + 1);
-          if (!VT && (i + 1) * kBlockKeys + kBlockKeys - 1 <= row0) {
+          if ((i + 1) * kBlockKeys + kBlockKeys - 1 <= row0) {
             // below the diagonal for every row of the wave: the matrix phase took the maxima
             bm[0] = bmx[0];
             bm[1] = bmx[1];
@@ -910,14 +1002,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
           }
           decide(false);
           codes(i + 1);
-        } else if constexpr (!VT) {
+        } else {
 #pragma unroll
           for (int n = 0; n < 2; ++n) {
             pb[n] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
             o_cur[n] = 0;
           }
         }
-        if (!VT || i + 2 < nb) wait_dma();
+        wait_dma();
         lds_barrier();
       }
       if (grp == 0) lds_barrier();
