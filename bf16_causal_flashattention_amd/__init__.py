@@ -79,8 +79,8 @@ def lib():
         L.attn_rotate_quantize_e4m3.argtypes = [P, P, P, I, I, I, I, P, P, P, P]
         L.attn_quantize_e4m3_static.argtypes = [P, I64, F, P, P]
         L.attn_rotate_quantize_e4m3_static.argtypes = [P, P, P, I, I, I, I, F, P, P]
-        L.attn_default_grid.argtypes = [I, I, I, I]
-        L.attn_schedule.argtypes = [I, I, I, I, P, I64]
+        L.attn_default_grid.argtypes = [I, I, I, I, I]
+        L.attn_schedule.argtypes = [I, I, I, I, I, P, I64]
         L.attn_schedule.restype = I64
         L.attn_status_string.argtypes = [I]
         L.attn_status_string.restype = ctypes.c_char_p
@@ -410,16 +410,17 @@ def round_bf16(x):
     return out.view(torch.bfloat16)
 
 
-def default_grid(B, H, S, num_cu):
-    return lib().attn_default_grid(B, H, S, num_cu)
+def default_grid(B, H, S, num_cu, Hkv=None):
+    return lib().attn_default_grid(B, H, H if Hkv is None else Hkv, S, num_cu)
 
 
-def schedule(B, H, S, grid):
-    """Execution-order (workgroup, b, h, tile) records of the persistent grid (host only)."""
+def schedule(B, H, S, grid, Hkv=None):
+    """Execution-order (workgroup, b, h, first row, rows) records of the persistent grid
+    (host only); with H / Hkv even a tile is 128 rows of two heads (two records)."""
     import numpy as np
-    T = S // 256
-    rec = np.zeros((B * H * T, 4), dtype=np.int32)
-    n = lib().attn_schedule(B, H, S, grid, ctypes.c_void_p(rec.ctypes.data), rec.shape[0])
+    rec = np.zeros((B * H * (S // 128), 5), dtype=np.int32)
+    n = lib().attn_schedule(B, H, H if Hkv is None else Hkv, S, grid, ctypes.c_void_p(rec.ctypes.data),
+                            rec.shape[0])
     if n < 0:
         raise AttnError("attn_schedule", int(n))
     return rec[:n]

@@ -147,8 +147,12 @@ int device_cu_count(int* n) {
   return ATTN_OK;
 }
 
-int grid_for(int B, int H, int S, int num_cu) {
-  const cfa::Schedule s = cfa::make_schedule(B, H, S);
+// the head-pair mode (Sec. IV-A): grouped-query attention with an even number of query
+// heads per key/value head
+bool pair_heads(int H, int Hkv) { return Hkv > 0 && H % Hkv == 0 && (H / Hkv) % 2 == 0; }
+
+int grid_for(int B, int H, int Hkv, int S, int num_cu) {
+  const cfa::Schedule s = cfa::make_schedule(B, H, S, pair_heads(H, Hkv));
   return (int)(s.items < num_cu ? s.items : num_cu);
 }
 
@@ -182,6 +186,7 @@ int run_fp8(const Problem& p, float qd, float kd, float vd, float sm, int p_mode
   a.H = p.H;
   a.S = p.S;
   a.G = p.H / p.Hkv;
+  a.pair_heads = pair_heads(p.H, p.Hkv) ? 1 : 0;
   a.mq = tmap(p.sq, 1);
   a.mk = tmap(p.sk, 1);
   a.mv = tmap(p.sv, 1);
@@ -191,7 +196,7 @@ int run_fp8(const Problem& p, float qd, float kd, float vd, float sm, int p_mode
   a.dbg_scores = dbg_s;
   const bool exact = p_mode == ATTN_P_EXACT || (p_mode == ATTN_P_DEFAULT && p.dqk == 192);
   const hipError_t e =
-      cfa::launch_fp8(a, p.dqk, exact, debug, p.v_channel_major, grid_for(p.B, p.H, p.S, ncu), (hipStream_t)stream);
+      cfa::launch_fp8(a, p.dqk, exact, debug, p.v_channel_major, grid_for(p.B, p.H, p.Hkv, p.S, ncu), (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -216,11 +221,12 @@ int run_bf16(const Problem& p, float sm, void* stream) {
   a.H = p.H;
   a.S = p.S;
   a.G = p.H / p.Hkv;
+  a.pair_heads = pair_heads(p.H, p.Hkv) ? 1 : 0;
   a.mq = tmap(p.sq, 2);
   a.mk = tmap(p.sk, 2);
   a.mv = tmap(p.sv, 2);
   a.mo = tmap(p.so, 2);
-  const hipError_t e = cfa::launch_bf16(a, p.dqk, grid_for(p.B, p.H, p.S, ncu), (hipStream_t)stream);
+  const hipError_t e = cfa::launch_bf16(a, p.dqk, grid_for(p.B, p.H, p.Hkv, p.S, ncu), (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -427,31 +433,39 @@ int attn_round_bf16(const float* x, int64_t n, uint16_t* out, void* stream) {
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
-int attn_default_grid(int B, int H, int S, int num_cu) {
-  if (B <= 0 || H <= 0 || S <= 0 || S % cfa::kTileRows != 0 || num_cu <= 0) return ATTN_ERR_SHAPE;
-  return grid_for(B, H, S, num_cu);
+int attn_default_grid(int B, int H, int H_kv, int S, int num_cu) {
+  if (B <= 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || S <= 0 || S % cfa::kTileRows != 0 || num_cu <= 0)
+    return ATTN_ERR_SHAPE;
+  return grid_for(B, H, H_kv, S, num_cu);
 }
 
-int64_t attn_schedule(int B, int H, int S, int grid, int32_t* records, int64_t cap) {
-  if (B <= 0 || H <= 0 || S <= 0 || S % cfa::kTileRows != 0 || grid <= 0) return ATTN_ERR_SHAPE;
-  const cfa::Schedule s = cfa::make_schedule(B, H, S);
-  const int64_t need = (int64_t)B * H * s.T;
+int64_t attn_schedule(int B, int H, int H_kv, int S, int grid, int32_t* records, int64_t cap) {
+  if (B <= 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || S <= 0 || S % cfa::kTileRows != 0 || grid <= 0)
+    return ATTN_ERR_SHAPE;
+  const bool pair = pair_heads(H, H_kv);
+  const cfa::Schedule s = cfa::make_schedule(B, H, S, pair);
+  const int rows = pair ? cfa::kPairTileRows : cfa::kTileRows, hstep = pair ? 2 : 1;
+  const int64_t need = (int64_t)B * H * (S / rows);
   if (!records || cap < need) return ATTN_ERR_ARG;
   int64_t n = 0;
   for (int bid = 0; bid < grid; ++bid) {
     const cfa::ItemRange work = cfa::xcd_items(bid, grid, s.items);
     for (int64_t item = work.first; item < work.end; item += work.step) {
-      int b, h, j;
-      cfa::decode_item(item, H, s.P, b, h, j);
+      int b, u, j;
+      cfa::decode_item(item, s.HS, s.P, b, u, j);
       for (int pass = 0; pass < 2; ++pass) {
         const int tile = pass == 0 ? s.T - 1 - j : j;
         if (pass == 1 && tile == s.T - 1 - j) break;
-        if (n >= need) return ATTN_ERR_ARG;  // would mean a tile is visited twice
-        records[4 * n + 0] = bid;
-        records[4 * n + 1] = b;
-        records[4 * n + 2] = h;
-        records[4 * n + 3] = tile;
-        ++n;
+        for (int e = 0; e < hstep; ++e) {
+          if (n >= need) return ATTN_ERR_ARG;  // would mean a tile is visited twice
+          int32_t* r = records + 5 * n;
+          r[0] = bid;
+          r[1] = b;
+          r[2] = hstep * u + e;
+          r[3] = tile * rows;
+          r[4] = rows;
+          ++n;
+        }
       }
     }
   }

@@ -156,7 +156,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
   const int lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
   const int grp = wave >> 2;
   const int S = a.S, H = a.H;
-  const Schedule sch = make_schedule(a.B, H, S);
+  // head-pair mode: a tile is 128 rows of each of the heads h (waves 0-3) and h+1 (waves 4-7)
+  const bool pair = a.pair_heads != 0;
+  const Schedule sch = make_schedule(a.B, H, S, pair);
+  const int hstep = pair ? 2 : 1;
+  const int trows = pair ? kPairTileRows : kTileRows;
+  const int wrow = pair ? (wave & 3) : wave;  // the wave's 32-row slot in the tile
   const ItemRange work = xcd_items(blockIdx.x, gridDim.x, sch.items);
   const int krs = a.mk.ss, vrs = a.mv.ss;  // key / value row strides in bytes
 
@@ -192,10 +197,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
   // (b, h, j) of the workgroup's first item; later items follow by scalar increments, so the
   // loop holds no division (whose reciprocals the compiler would keep in vector registers)
   int b, h, j;
-  decode_item(work.first, H, sch.P, b, h, j);
+  decode_item(work.first, sch.HS, sch.P, b, h, j);
+  h *= hstep;
   int hk = h / a.G, hg = h - hk * a.G;  // key/value head of query head h, and h's place in its group
   for (int64_t item = work.first; item < work.end; item += work.step) {
-    const uint8_t* qbh = (const uint8_t*)a.q + b * a.mq.sb + h * a.mq.sh;
+    const int hw = h + (pair ? grp : 0);  // the wave's query head
+    const uint8_t* qbh = (const uint8_t*)a.q + b * a.mq.sb + hw * a.mq.sh;
     const uint8_t* st_head = stage_k ? (const uint8_t*)a.k + b * a.mk.sb + hk * a.mk.sh
                                      : (const uint8_t*)a.v + b * a.mv.sb + hk * a.mv.sh;
     const int st_rs = stage_k ? krs : vrs;
@@ -205,9 +212,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
       // together and read the same K/V blocks from its L2 for most of that tile
       const int tile = pass == 0 ? sch.T - 1 - j : j;
       if (pass == 1 && tile == sch.T - 1 - j) break;
-      const int row0 = tile * kTileRows + wave * kWaveRows;
+      const int row0 = tile * trows + wrow * kWaveRows;
       const int qrow = row0 + l32;
-      const int nb = (tile + 1) * (kTileRows / kBlk);  // key blocks
+      const int nb = (tile + 1) * (trows / kBlk);  // key blocks
 
       // DMA of block blk: K into slot blk % 2, V into slot blk % kVS.  stage() goes through a
       // scalar base (copy_round: no per-lane 64-bit addresses, which the compiler would keep,
@@ -372,7 +379,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
 
       // prologue: only the Q rows and block 0 are waited for before the first barrier; block 1
       // streams in under the first two phases, each wave waiting for its share at the end of
-      // its S_pro (K(1) is first read in M_0, V(1) in S_0)
+      // its S_pro (K(1) is first read in M_0, V(1) in S_0).  Tile 0 of the head-pair mode at
+      // d_qk = 128 has one block; its block 1 (keys 128-255, present since S >= 256) is copied
+      // unused.
       stage(0);
       wait_dma();
       lds_barrier();
@@ -437,7 +446,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
           *(uint2*)(stg + l32 * kStgPitch + 2 * d0) = w;
         }
       {
-        uint8_t* orow = (uint8_t*)a.out + b * a.mo.sb + h * a.mo.sh + (int64_t)row0 * a.mo.ss;
+        uint8_t* orow = (uint8_t*)a.out + b * a.mo.sb + hw * a.mo.sh + (int64_t)row0 * a.mo.ss;
         const int ln = lane_now();
         const int sr = ln >> 4, sc = 16 * (ln & 15);
 #pragma unroll
@@ -446,7 +455,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
           *(v4i*)(orow + (int64_t)r * a.mo.ss + sc) = *(const v4i*)(stg + r * kStgPitch + sc);
         }
       }
-      if (a.lse != nullptr && hh == 0) a.lse[(int64_t)(b * H + h) * S + qrow] = kLn2 * (m + __log2f(lt));
+      if (a.lse != nullptr && hh == 0) a.lse[(int64_t)(b * H + hw) * S + qrow] = kLn2 * (m + __log2f(lt));
       lds_barrier();
     }
     // the workgroup's next item, work.step items on
@@ -454,11 +463,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
     j += work.step;
     while (j >= sch.P) {
       j -= sch.P;
-      if (++hg == a.G) {
+      hg += hstep;
+      if (hg == a.G) {
         hg = 0;
         ++hk;
       }
-      if (++h == H) {
+      h += hstep;
+      if (h == H) {
         h = hg = hk = 0;
         ++b;
       }

@@ -19,8 +19,12 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 // A workgroup owns a tile of 256 query rows; each of its 8 waves owns 32 rows
-// (two waves per SIMD).  Keys stream through LDS in blocks of 128 (FP8) or 64 (BF16).
+// (two waves per SIMD).  Keys stream through LDS in blocks of 128 (FP8 and BF16 at
+// d_qk = 128) or 64 (BF16 at d_qk = 192).  In the head-pair mode (grouped-query
+// attention with an even group) a tile is 128 rows of each of two query heads that share
+// one key/value head: waves 0-3 take the first head, waves 4-7 the second.
 constexpr int kTileRows = 256;
+constexpr int kPairTileRows = 128;
 constexpr int kWaves = 8;
 constexpr int kWaveRows = 32;
 constexpr int kThreads = 512;
@@ -42,17 +46,27 @@ constexpr int kXcds = 8;
 // So the workgroups of one XCD always work on neighbouring items, the tile pairs of one
 // or two heads, whose K and V blocks then stream through that XCD's L2 once.  The ranges
 // follow the workgroup counts, so no workgroup gets more than ceil(N / G) items.
+//
+// Head-pair mode (Sec. IV-A: with grouped-query attention and an even group size a pair
+// covers two query heads with tiles of half the size).  The heads 2u and 2u+1, which share
+// a key/value head, form head pair u; its tiles have 128 rows of each head, T = S / 128,
+// and the items are numbered as above with H/2 head pairs in place of H heads.  Every K/V
+// block a workgroup stages then feeds 256 query rows of two heads, and a tile has one
+// diagonal block instead of two, so a pair takes S/128 + 1 block steps instead of S/128 + 2.
 struct Schedule {
-  int T;          // tiles per head
-  int P;          // items per head
-  int64_t items;  // B * H * P
+  int T;          // tiles per head (per head pair in the head-pair mode)
+  int P;          // items per head (per head pair)
+  int HS;         // heads (head pairs) the items run over
+  int64_t items;  // B * HS * P
 };
 
-__host__ __device__ inline Schedule make_schedule(int B, int H, int S) {
+// pair_heads: the head-pair mode, for H / H_kv even
+__host__ __device__ inline Schedule make_schedule(int B, int H, int S, bool pair_heads) {
   Schedule s;
-  s.T = S / kTileRows;
+  s.T = S / (pair_heads ? kPairTileRows : kTileRows);
   s.P = (s.T + 1) / 2;
-  s.items = (int64_t)B * H * s.P;
+  s.HS = pair_heads ? H / 2 : H;
+  s.items = (int64_t)B * s.HS * s.P;
   return s;
 }
 
@@ -81,6 +95,7 @@ __host__ __device__ inline ItemRange xcd_items(int bid, int grid, int64_t items)
   return r;
 }
 
+// (b, head or head pair u, j) of an item, for HS heads (head pairs) and P items per head
 __host__ __device__ inline void decode_item(int64_t item, int H, int P, int& b, int& h, int& j) {
   const int64_t bh = item / P;
   j = (int)(item - bh * P);

@@ -140,7 +140,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
   const int lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
   const int grp = wave >> 2;  // 0: waves 0-3, 1: waves 4-7 (one of each per SIMD)
   const int S = a.S, H = a.H;
-  const Schedule sch = make_schedule(a.B, H, S);
+  // head-pair mode: a tile is 128 rows of each of the heads h (waves 0-3) and h+1 (waves 4-7)
+  const bool pair = a.pair_heads != 0;
+  const Schedule sch = make_schedule(a.B, H, S, pair);
+  const int hstep = pair ? 2 : 1;
+  const int trows = pair ? kPairTileRows : kTileRows;
+  const int wrow = pair ? (wave & 3) : wave;  // the wave's 32-row slot in the tile
   const ItemRange work = xcd_items(blockIdx.x, gridDim.x, sch.items);
 
   // key row stride in bytes; value row stride (key-major V) or channel row stride (VT)
@@ -201,10 +206,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
   // (b, h, j) of the workgroup's first item; later items follow by scalar increments, so the
   // loop holds no division (whose reciprocals the compiler would keep in vector registers)
   int b, h, j;
-  decode_item(work.first, H, sch.P, b, h, j);
+  decode_item(work.first, sch.HS, sch.P, b, h, j);
+  h *= hstep;
   int hk = h / a.G, hg = h - hk * a.G;  // key/value head of query head h, and h's place in its group
   for (int64_t item = work.first; item < work.end; item += work.step) {
-    const uint8_t* qbh = a.q + b * a.mq.sb + h * a.mq.sh;
+    const int hw = h + (pair ? grp : 0);  // the wave's query head
+    const uint8_t* qbh = a.q + b * a.mq.sb + hw * a.mq.sh;
     const uint8_t* st_head = stage_k ? a.k + b * a.mk.sb + hk * a.mk.sh : a.v + b * a.mv.sb + hk * a.mv.sh;
     // bytes from one 128-key block to the next in the staged tensor
     const int64_t st_bstep = stage_k || !VT ? (int64_t)kBlockKeys * (stage_k ? krs : vrs) : kBlockKeys;
@@ -214,9 +221,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
       // together and read the same K/V blocks from its L2 for most of that tile
       const int tile = pass == 0 ? sch.T - 1 - j : j;
       if (pass == 1 && tile == sch.T - 1 - j) break;
-      const int row0 = tile * kTileRows + wave * kWaveRows;  // first query row of this wave
+      const int row0 = tile * trows + wrow * kWaveRows;  // first query row of this wave
       const int qrow = row0 + l32;
-      const int nb = 2 * tile + 2;                             // 128-key blocks
+      const int nb = pair ? tile + 1 : 2 * tile + 2;       // 128-key blocks
 
       // DMA of block blk: K by group 0 into slot blk % 2, V by group 1 into slot blk % 3
       auto stage = [&](int blk) {
@@ -848,7 +855,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
         const int key0 = blk * kBlockKeys;
         if constexpr (DEBUG) {  // raw scores as the MFMA left them, before the mask
           if (a.dbg_scores != nullptr) {
-            float* srow = a.dbg_scores + ((int64_t)(b * H + h) * S + qrow) * S + key0 + 16 * hh;
+            float* srow = a.dbg_scores + ((int64_t)(b * H + hw) * S + qrow) * S + key0 + 16 * hh;
 #pragma unroll
             for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -936,8 +943,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
         o_cur[1] = o_nxt[1];
         if constexpr (DEBUG) {
           const int key0 = blk * kBlockKeys;
-          uint8_t* orow = a.dbg_o + ((int64_t)(b * H + h) * S + qrow) * (S / 64);
-          uint8_t* crow = a.dbg_codes + ((int64_t)(b * H + h) * S + qrow) * S;
+          uint8_t* orow = a.dbg_o + ((int64_t)(b * H + hw) * S + qrow) * (S / 64);
+          uint8_t* crow = a.dbg_codes + ((int64_t)(b * H + hw) * S + qrow) * S;
           if (hh == 0) {
             orow[key0 / 64] = (uint8_t)o_cur[0];
             orow[key0 / 64 + 1] = (uint8_t)o_cur[1];
@@ -956,7 +963,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
       // K(0), K(1) by group 0 and V(0), V(1) by group 1.  Only the Q rows and block 0 are
       // waited for here: block 1 streams in under the first two phases and each wave waits
       // for its share at the end of its S_pro (K(1) is first read in M_0, V(1) in M_1), so a
-      // tile starts after one block's copies instead of two.
+      // tile starts after one block's copies instead of two.  Tile 0 of the head-pair mode
+      // has one block; its block 1 (keys 128-255, present since S >= 256) is copied unused.
       stage(0);
       wait_dma();
       lds_barrier();
@@ -1032,7 +1040,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
           *(uint2*)(stg + l32 * kStgPitch + 2 * d0) = w;
         }
       {
-        uint8_t* orow = (uint8_t*)a.out + b * a.mo.sb + h * a.mo.sh + (int64_t)row0 * a.mo.ss;
+        uint8_t* orow = (uint8_t*)a.out + b * a.mo.sb + hw * a.mo.sh + (int64_t)row0 * a.mo.ss;
         const int ln = lane_now();
         const int sr = ln >> 4, sc = 16 * (ln & 15);
 #pragma unroll
@@ -1042,7 +1050,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
         }
       }
       if (a.lse != nullptr && hh == 0)
-        a.lse[(int64_t)(b * H + h) * S + qrow] = kLn2 * (m + __log2f(l) - (float)kSigma);
+        a.lse[(int64_t)(b * H + hw) * S + qrow] = kLn2 * (m + __log2f(l) - (float)kSigma);
       lds_barrier();
     }
     // the workgroup's next item, work.step items on
@@ -1050,11 +1058,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
     j += work.step;
     while (j >= sch.P) {
       j -= sch.P;
-      if (++hg == a.G) {
+      hg += hstep;
+      if (hg == a.G) {
         hg = 0;
         ++hk;
       }
-      if (++h == H) {
+      h += hstep;
+      if (h == H) {
         h = hg = hk = 0;
         ++b;
       }

@@ -24,6 +24,7 @@ struct Fp8Args {
   float v_descale;
   int B, H, S;
   int G;             // query heads per key/value head (H / H_kv): head h reads key/value head h / G
+  int pair_heads;    // 1: head-pair mode (G even), a tile is 128 rows of heads 2u and 2u+1
   TensorMap mq, mk, mv, mo;
   uint8_t* dbg_o;      // debug build only: [B*H*S][S/64] block exponents
   uint8_t* dbg_codes;  // debug build only: [B*H*S][S] probability codes
@@ -39,6 +40,7 @@ struct Bf16Args {
   float cp;  // fp32(softmax_scale * log2 e)
   int B, H, S;
   int G;
+  int pair_heads;  // as in Fp8Args
   TensorMap mq, mk, mv, mo;
 };
 

@@ -229,15 +229,20 @@ int attn_fwd_causal_fp8_debug_ex(const void* q, const void* k, const void* v, vo
                                  const attn_strides* out_strides, int p_mode, uint8_t* dbg_o, uint8_t* dbg_codes,
                                  float* dbg_scores, void* stream);
 
-/* Host-only helpers (no device call), for schedule inspection and tests.
+/* Host-only helpers (no device call), for schedule inspection and tests (ZYFA paper,
+ * Sec. IV-A: causal pairing, persistent grid, chiplet placement).
  * attn_default_grid: the persistent grid the attention entry points launch for a
- *   problem on a device with num_cu compute units: min(num_cu, work items).
- * attn_schedule: writes, in execution order, one (workgroup, b, h, tile) record of
- *   four int32 per query tile that the grid of `grid` workgroups processes; returns
- *   the number of records (B*H*S/256), or a negative attn_status if `cap` records do
- *   not fit or the sizes are invalid. */
-int attn_default_grid(int B, int H, int S, int num_cu);
-int64_t attn_schedule(int B, int H, int S, int grid, int32_t* records, int64_t cap);
+ *   problem with H query and H_kv key/value heads on a device with num_cu compute
+ *   units: min(num_cu, work items).
+ * attn_schedule: writes, in execution order, one (workgroup, b, h, first query row,
+ *   rows) record of five int32 per query tile and head that the grid of `grid`
+ *   workgroups processes.  When H / H_kv is even the kernels run the head-pair mode
+ *   (Sec. IV-A: a pair covers two query heads with tiles of half the size): a tile is
+ *   128 rows of heads 2u and 2u+1, recorded as two consecutive records; otherwise a
+ *   tile is 256 rows of one head.  Returns the number of records (B*H*S/rows), or a
+ *   negative attn_status if `cap` records do not fit or the sizes are invalid. */
+int attn_default_grid(int B, int H, int H_kv, int S, int num_cu);
+int64_t attn_schedule(int B, int H, int H_kv, int S, int grid, int32_t* records, int64_t cap);
 
 /* Human-readable name of a status code. */
 const char* attn_status_string(int status);

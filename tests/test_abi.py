@@ -248,51 +248,76 @@ def test_status_strings():
     assert b"unknown" in L.attn_status_string(-99)
 
 
-@pytest.mark.parametrize("B,H,S,grid", [(1, 1, 256, 1), (1, 32, 32768, 256), (2, 3, 1280, 7), (1, 16, 32768, 256),
-                                        (4, 5, 2048, 13), (1, 1, 768, 256), (3, 2, 2560, 256)])
-def test_schedule_covers_every_tile_once(B, H, S, grid):
-    T = S // 256
-    g = min(grid, cfa.default_grid(B, H, S, grid))
-    rec = cfa.schedule(B, H, S, g)
+@pytest.mark.parametrize("B,H,Hkv,S,grid", [(1, 1, 1, 256, 1), (1, 32, 32, 32768, 256), (2, 3, 3, 1280, 7),
+                                            (1, 16, 16, 32768, 256), (4, 5, 5, 2048, 13), (1, 1, 1, 768, 256),
+                                            (3, 2, 2, 2560, 256), (1, 32, 8, 32768, 256), (2, 6, 3, 1280, 7),
+                                            (1, 2, 1, 256, 1), (3, 8, 2, 2560, 256), (1, 6, 2, 768, 5),
+                                            (2, 4, 4, 512, 3)])
+def test_schedule_covers_every_tile_once(B, H, Hkv, S, grid):
+    """Every 128-row strip of every (b, h) is processed exactly once; workgroups get balanced
+    work; each item is a causal pair (j, T-1-j) of one head, or of the two heads 2u, 2u+1 of a
+    head pair with 128-row tiles when H / Hkv is even (ZYFA paper, Sec. IV-A)."""
+    pair = (H // Hkv) % 2 == 0
+    R = 128 if pair else 256
+    T = S // R
+    g = min(grid, cfa.default_grid(B, H, S, grid, Hkv=Hkv))
+    rec = cfa.schedule(B, H, S, g, Hkv=Hkv)
     assert rec.shape[0] == B * H * T
-    seen = np.zeros((B, H, T), dtype=np.int64)
-    np.add.at(seen, (rec[:, 1], rec[:, 2], rec[:, 3]), 1)
+    assert np.all(rec[:, 4] == R) and np.all(rec[:, 3] % R == 0)
+    seen = np.zeros((B, H, S // 128), dtype=np.int64)
+    for r in range(R // 128):
+        np.add.at(seen, (rec[:, 1], rec[:, 2], rec[:, 3] // 128 + r), 1)
     assert np.all(seen == 1)
-    # work per workgroup in 256-key steps: tile t costs t+1; pairs (j, T-1-j) cost T+1
-    work = np.zeros(g, dtype=np.int64)
-    np.add.at(work, rec[:, 0], rec[:, 3] + 1)
-    items = B * H * ((T + 1) // 2)
+    # a tile of R rows at tile index t takes (t+1) R / 128 steps of 128 keys; in the head-pair
+    # mode its two records (one per head) share those steps
+    steps = (rec[:, 3] // R + 1) * (R // 128)
+    share = 0.5 if pair else 1.0
+    work = np.zeros(g, dtype=np.float64)
+    np.add.at(work, rec[:, 0], steps * share)
+    hs = H // 2 if pair else H
+    items = B * hs * ((T + 1) // 2)
     per = math.ceil(items / g)
-    assert work.max() <= per * (T + 1)
-    # consecutive tiles of a workgroup alternate j, T-1-j within one head
+    assert work.max() <= per * (T + 1) * (R // 128)
+    # consecutive tiles of a workgroup: (j, T-1-j), for one head or for the heads 2u, 2u+1
+    n = 2 if pair else 1
     for wg in range(min(g, 4)):
         r = rec[rec[:, 0] == wg]
+        assert len(r) % n == 0
+        tiles = r[::n]
+        for e in range(1, n):  # the second head of each pair tile
+            assert np.all(r[e::n, 2] == tiles[:, 2] + e) and np.all(r[e::n, 3] == tiles[:, 3])
+            assert np.all(tiles[:, 2] % 2 == 0)
         i = 0
-        while i < len(r):
-            if r[i, 3] == T - 1 - r[i, 3]:  # middle tile of an odd T runs alone
+        while i < len(tiles):
+            t = tiles[i, 3] // R
+            if t == T - 1 - t:  # middle tile of an odd T runs alone
                 i += 1
                 continue
-            assert r[i + 1, 3] == T - 1 - r[i, 3] and r[i + 1, 1] == r[i, 1] and r[i + 1, 2] == r[i, 2]
+            nxt = tiles[i + 1]
+            assert nxt[3] // R == T - 1 - t and nxt[1] == tiles[i, 1] and nxt[2] == tiles[i, 2]
             i += 2
 
 
-def test_xcd_remap_is_contiguous_per_chiplet():
+@pytest.mark.parametrize("Hkv", [32, 8])
+def test_xcd_remap_is_contiguous_per_chiplet(Hkv):
     # workgroup i runs on chiplet i % 8; its first item should be a contiguous run per chiplet
     B, H, S, g = 1, 32, 32768, 256
-    rec = cfa.schedule(B, H, S, g)
+    rec = cfa.schedule(B, H, S, g, Hkv=Hkv)
     first = {}
-    for wg, b, h, t in rec:
+    for wg, b, h, r0, rows in rec:
         if wg not in first:
-            first[wg] = (h, min(t, S // 256 - 1 - t))
+            first[wg] = h
     for x in range(8):
-        heads = {first[wg][0] for wg in range(x, g, 8)}
-        assert len(heads) == 1  # 32 workgroups of one chiplet start on one head
+        heads = {first[wg] for wg in range(x, g, 8)}
+        assert len(heads) == 1  # 32 workgroups of one chiplet start on one head (head pair)
 
 
 def test_default_grid():
     assert cfa.default_grid(1, 32, 32768, 256) == 256
     assert cfa.default_grid(1, 1, 256, 256) == 1
     assert cfa.default_grid(1, 1, 300, 256) == -2
+    assert cfa.default_grid(1, 2, 256, 256, Hkv=1) == 1  # one head pair, one 128-row tile pair
+    assert cfa.default_grid(1, 4, 512, 256, Hkv=3) == -2  # H not a multiple of H_kv
 
 
 def test_binding_rejects_host_tensors_before_any_call():

@@ -271,13 +271,15 @@ def _bf16_ex_check(q, k, v, layout):
 
 
 @pytest.mark.parametrize("kind,dqk", [("fp8", 128), ("fp8", 192), ("bf16", 128), ("bf16", 192)])
-@pytest.mark.parametrize("B,H,Hkv,S", [(3, 96, 48, 512), (2, 10, 5, 8192)])
+@pytest.mark.parametrize("B,H,Hkv,S", [(3, 96, 48, 512), (2, 10, 5, 8192), (2, 9, 3, 1024), (1, 8, 2, 2048)])
 def test_many_items_per_workgroup(kind, dqk, B, H, Hkv, S):
     """More tile pairs than workgroups (288 and 320 items for at most 256 workgroups), over
     several batches and grouped key/value heads: a workgroup then steps through several work
     items, from one pair of a head to the next (S = 8192, 16 pairs per head) and across heads
     and batches (S = 512, one pair per head).  A causal row does not depend on which workgroup
-    runs it, so every (b, h) of the launch must equal a launch on that head alone, bit for bit."""
+    runs it, so every (b, h) of the launch must equal a launch on that head alone, bit for bit.
+    With an even group (G = 2, 4) the launch runs the head-pair mode (two heads, 128-row tiles)
+    and the single-head launches do not; G = 3 runs 256-row tiles of one head."""
     _case("many items per workgroup", kind, dqk, B, H, Hkv, S)
     G = H // Hkv
     q, k, v = _inputs(B, H, Hkv, S, dqk, seed=B * H + S + dqk)
