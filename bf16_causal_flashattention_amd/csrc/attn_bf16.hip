@@ -200,9 +200,38 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
   decode_item(work.first, sch.HS, sch.P, b, h, j);
   h *= hstep;
   int hk = h / a.G, hg = h - hk * a.G;  // key/value head of query head h, and h's place in its group
-  for (int64_t item = work.first; item < work.end; item += work.step) {
+  // the item after (b, h, j): work.step items on
+  auto next_item = [&](int& b_, int& h_, int& hk_, int& hg_, int& j_) {
+    j_ += work.step;
+    while (j_ >= sch.P) {
+      j_ -= sch.P;
+      hg_ += hstep;
+      if (hg_ == a.G) {
+        hg_ = 0;
+        ++hk_;
+      }
+      h_ += hstep;
+      if (h_ == H) {
+        h_ = hg_ = hk_ = 0;
+        ++b_;
+      }
+    }
+  };
+  // Q^T operand (lane holds Q[qrow][16m + 8hh .. +8]) of a tile: the first tile's here, every
+  // later one's at the start of the epilogue before it, so the load overlaps that epilogue
+  v4i qop[QM];
+  auto load_q = [&](int b_, int h_, int tile_) {
+    const uint8_t* qh = (const uint8_t*)a.q + b_ * a.mq.sb + (h_ + (pair ? grp : 0)) * a.mq.sh;
+    const int ln = lane_now();
+    const uint8_t* qp = qh + (int64_t)(tile_ * trows + wrow * kWaveRows + (ln & 31)) * a.mq.ss + 16 * (ln >> 5);
+#pragma unroll
+    for (int mm = 0; mm < QM; ++mm) qop[mm] = *(const v4i*)(qp + 32 * mm);
+  };
+  // item indices fit in 32 bits (B H S is below 2^31 / d_qk); a 32-bit loop bound stays scalar
+  const int wfirst = (int)work.first, wend = (int)work.end;
+  if (wfirst < wend) load_q(b, h, sch.T - 1 - j);
+  for (int item = wfirst; item < wend; item += work.step) {
     const int hw = h + (pair ? grp : 0);  // the wave's query head
-    const uint8_t* qbh = (const uint8_t*)a.q + b * a.mq.sb + hw * a.mq.sh;
     const uint8_t* st_head = stage_k ? (const uint8_t*)a.k + b * a.mk.sb + hk * a.mk.sh
                                      : (const uint8_t*)a.v + b * a.mv.sb + hk * a.mv.sh;
     const int st_rs = stage_k ? krs : vrs;
@@ -239,13 +268,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
           if (256 * p + 64 * wq < st_cells) dma16(src + st_goff[p], dst + 4096 * p);
       };
 
-      v4i qop[QM];  // Q^T operand: lane holds Q[qrow][16m + 8hh .. +8]
-      {
-        const int ln = lane_now();
-        const uint8_t* qp = qbh + (int64_t)(row0 + (ln & 31)) * a.mq.ss + 16 * (ln >> 5);
-#pragma unroll
-        for (int m = 0; m < QM; ++m) qop[m] = *(const v4i*)(qp + 32 * m);
-      }
       v16f oacc[4];
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) oacc[dt] = zero16;
@@ -432,6 +454,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
 
       // epilogue: O through a per-wave LDS staging area, stored as whole 256-byte rows (the
       // barrier at the end keeps the next tile's copies out until every wave has read its area)
+      if (pass == 0 && j != sch.T - 1 - j) {
+        load_q(b, h, j);
+      } else if (item + work.step < wend) {
+        int b1 = b, h1 = h, hk1 = hk, hg1 = hg, j1 = j;
+        next_item(b1, h1, hk1, hg1, j1);
+        load_q(b1, h1, sch.T - 1 - j1);
+      }
       const float lt = sum_with_partner(l);
       const float inv = 1.0f / lt;
       uint8_t* stg = smem + wave * kStgWave;
@@ -459,21 +488,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(Bf16Args a) 
       lds_barrier();
     }
     // the workgroup's next item, work.step items on
-    if (item + work.step >= work.end) break;
-    j += work.step;
-    while (j >= sch.P) {
-      j -= sch.P;
-      hg += hstep;
-      if (hg == a.G) {
-        hg = 0;
-        ++hk;
-      }
-      h += hstep;
-      if (h == H) {
-        h = hg = hk = 0;
-        ++b;
-      }
-    }
+    if (item + work.step >= wend) break;
+    next_item(b, h, hk, hg, j);
   }
 }
 
