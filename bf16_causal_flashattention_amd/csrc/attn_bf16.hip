@@ -4,8 +4,9 @@
 //   Sec. II-B  base-2 online softmax over key blocks (128 keys at d_qk = 128, as the paper
 //              prices a BF16 block in Table III; 64 at the MLA shape), LSE output;
 //   Sec. IV-A  8 waves x 32 query rows, S^T = K Q^T so each lane holds one query's
-//              scores, causal pairing, persistent grid, chiplet map, lazy rescaling
-//              with tau = 4 at d_qk = 128 and 8 at the MLA shape d_qk = 192;
+//              scores, causal pairing (with grouped-query attention and an even group, a
+//              tile is 128 rows of each of two query heads), persistent grid, chiplet map,
+//              lazy rescaling with tau = 4 at d_qk = 128 and 8 at the MLA shape d_qk = 192;
 //   Sec. VI-A  dead-block skip: in the diagonal blocks a wave skips the key blocks
 //              that the causal mask hides from all its rows (loads and barriers still run);
 //   Sec. IV-D  the 8-wave ping-pong of the BF16 d = 128 kernel: the two waves of a SIMD
@@ -30,8 +31,8 @@
 // has closed both groups' reads of V(i).  Each wave waits for its copies at the end of S_i.
 // Every target slot was last read before the copy's issuing barrier and every copy
 // completes at least one phase before its first read.
-// The epilogue stores O as whole rows through a per-wave LDS staging area, as in the FP8
-// kernel.
+// The epilogue first requests the Q rows of the wave's next tile, then stores O as whole rows
+// through a per-wave LDS staging area, as in the FP8 kernel.
 //
 // fp32 arithmetic: t = s * cp with cp = fp32(c log2 e); p = exp2(fmaf(s, cp, -m));
 // l sums the fp32 p; P is p rounded to bf16; O = bf16(acc / l); LSE = ln 2 (m + log2 l).

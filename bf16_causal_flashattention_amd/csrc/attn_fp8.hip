@@ -15,13 +15,14 @@
 //                      the paper's MFMA wave does, takes the block maxima of the next block
 //                      between its PV MFMAs.
 //
-// Schedule per 256-row tile with nb 128-key blocks.  Group g = wave / 4 (one wave of
-// each group per SIMD).  Group 1 runs one phase behind group 0:
+// Schedule per tile (256 rows of one head, or in the head-pair mode 128 rows of each of two
+// heads that share a key/value head) with nb 128-key blocks.  Group g = wave / 4 (one wave
+// of each group per SIMD).  Group 1 runs one phase behind group 0:
 //   group 0:  M_pro S_pro M_0 S_0 M_1 S_1 ... M_{nb-1} S_{nb-1} idle
 //   group 1:  idle  M_pro S_pro M_0 S_0 ... M_{nb-1} S_{nb-1}
 // M_i (matrix phase): row sums of P(i); S(i+1) = K(i+1) Q^T; O += V(i)^T P(i); l update;
 //      the block maxima of S(i+1) (the softmax phase redoes them with the causal mask on the
-//      two diagonal blocks of a tile).
+//      blocks that cross a wave's diagonal).
 // S_i (softmax phase): the masked block maxima on the diagonal, lazy decision (and the rare
 //      rescale of O and l), o(i+1), P(i+1).
 // Staging by DMA (global_load_lds, no registers): at the end of M_i, after its last
@@ -32,10 +33,11 @@
 // LDS, so nothing waits on a copy early.  Every step copies: in a tile's last two steps,
 // which have no block i+2, the wave copies the tile's last block again into the slot the
 // schedule frees.
-// Epilogue: after the tile's last barrier no wave reads K or V, so each wave writes its
-// 32 rows of bf16 O into a staging area of its own at the start of LDS and stores them
-// as whole 256-byte rows; a barrier keeps the next tile's copies out until every wave
-// has read its area.
+// Epilogue: after the tile's last barrier no wave reads K or V, so each wave first requests
+// the Q rows of its next tile (the operand registers are free now), then writes its 32 rows
+// of bf16 O into a staging area of its own at the start of LDS and stores them as whole
+// 256-byte rows; a barrier keeps the next tile's copies out until every wave has read its
+// area.
 //
 // fp32 arithmetic (the order below is part of the contract with the test oracle):
 //   cp   = fp32(c * dq * dk * log2 e), scores s are fp32 MFMA sums
