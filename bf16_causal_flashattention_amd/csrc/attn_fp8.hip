@@ -104,8 +104,13 @@ struct Fp8Lds {
   static constexpr int kVSlot = 16 * kVCells;
   // byte offsets of the transpose reads (see v_row_of_key): the 64 keys of scale block n start
   // 8448 n bytes in; the four 8-key pieces of a lane half at keys +0, +8, +32, +40 lie 0, 256,
-  // 4224 and 4480 bytes from the first
+  // 4224 and 4480 bytes from the first.  The matrix-phase assembly writes these offsets as
+  // literals; the asserts below tie them to the placement.
   static constexpr int kVHalf = 8448, kVPc8 = 256, kVPc32 = 4224, kVPc40 = 4480;
+  static_assert(v_row_offset(v_row_of_key(64)) == kVHalf && v_row_offset(v_row_of_key(8)) == kVPc8 &&
+                    v_row_offset(v_row_of_key(32)) == kVPc32 && v_row_offset(v_row_of_key(40)) == kVPc40 &&
+                    v_row_offset(v_row_of_key(0)) == 0,
+                "transpose-read offsets of the matrix-phase assembly do not match the V placement");
   static constexpr int kVBase = 2 * kKSlot;
   static constexpr int kBytes = 2 * kKSlot + 3 * kVSlot;
   static constexpr int kRounds = ((kKCells > kVCells ? kKCells : kVCells) + 255) / 256;  // DMA rounds, 256 threads
@@ -321,6 +326,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
       // it may come just before the block), two after the selector moves and after the
       // permlane operands are written, one after each M0 write; the instructions after the last
       // PV MFMA cover the 20 that a VALU read of its results needs.
+      // the assembly below writes the LDS strides as literal offsets: 32 K rows (one sub-tile)
+      // are 4608 bytes at d_qk = 128 and 6656 at 192, 32 channel rows of channel-major V 4608
+      static_assert(32 * L::kKStride == (DQK == 128 ? 4608 : 6656), "K sub-tile stride of the matrix-phase assembly");
+      static_assert(32 * 16 * L::kVtSpr == 4608, "channel-row stride of the matrix-phase assembly");
       float bmx[2] = {0.f, 0.f};  // block maxima of the next block from the hand-ordered matrix phase
       float bm[2];
       auto mphase_asm = [&](int i) -> v2f {
