@@ -205,6 +205,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
   // iff (L/16)%2 == ((L%16)/4)%2, so every lane receives the sum of its own query.
   const int sel_on = (((lane >> 4) & 1) == (((lane & 15) >> 2) & 1));
   const int selw = sel_on ? 0x38383838 : 0;
+  const v8i selv = {selw, selw, selw, selw, selw, selw, selw, selw};
   const v16f zero16 = {};
 
   const float cp = a.cp;
@@ -319,13 +320,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
       // QK^T MFMAs; every read is waited for inside the block.  A V^T operand is four
       // transpose reads from key-major V, or two 16-byte reads from channel-major V (the
       // assembler's .if on the vt operand picks one).  K and V^T operands pass through
-      // two fixed 8-register groups (v240-v255; the second carries the 0/1 row-sum selector
-      // first), and the scores sit in v176-v239 so that the maxima can name them.  Copies go
-      // through a scalar base and the per-lane 32-bit offsets, with M0 saved and restored.
-      // Wait states: five before the first copy may read the scalar base (a compiler reload of
-      // it may come just before the block), two after the selector moves and after the
-      // permlane operands are written, one after each M0 write; the instructions after the last
-      // PV MFMA cover the 20 that a VALU read of its results needs.
+      // two fixed 8-register groups (v240-v255), the 0/1 row-sum selector is an input that stays
+      // in registers across the loop, and the scores sit in v176-v239 so that the maxima can
+      // name them.  Copies go through a scalar base and the per-lane 32-bit offsets, with M0
+      // saved and restored.  Wait states: five at the top, before the first copy may read the
+      // scalar base (a compiler reload of it may come just before the block) and before the
+      // row-sum MFMAs read the selector and the codes, two after the permlane operands are
+      // written, one after each M0 write; the instructions after the last PV MFMA cover the 20
+      // that a VALU read of its results needs.
       // the assembly below writes the LDS strides as literal offsets: 32 K rows (one sub-tile)
       // are 4608 bytes at d_qk = 128 and 6656 at 192, 32 channel rows of channel-major V 4608
       static_assert(32 * L::kKStride == (DQK == 128 ? 4608 : 6656), "K sub-tile stride of the matrix-phase assembly");
@@ -354,20 +356,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
             "s_nop 4\n\t"
             "s_mov_b32 %[m0s], m0\n\t"
             "s_waitcnt lgkmcnt(0)\n\t"
-            // row sums of P(i): the 0/1 selector in group 1, the first K operand read in group 0
-            "v_mov_b32 v248, %[selw]\n\t"
-            "v_mov_b32 v249, %[selw]\n\t"
-            "v_mov_b32 v250, %[selw]\n\t"
-            "v_mov_b32 v251, %[selw]\n\t"
-            "v_mov_b32 v252, %[selw]\n\t"
-            "v_mov_b32 v253, %[selw]\n\t"
-            "v_mov_b32 v254, %[selw]\n\t"
-            "v_mov_b32 v255, %[selw]\n\t"
+            // row sums of P(i) against the 0/1 selector; the first K operand read in group 0
             "ds_read_b128 v[240:243], %[kb]\n\t"
             "ds_read_b128 v[244:247], %[kb] offset:16\n\t"
-            "s_nop 1\n\t"
-            "v_mfma_scale_f32_16x16x128_f8f6f4 %[b0], v[248:255], %[p0], 0, %[one], %[one] op_sel_hi:[0,0,0]\n\t"
-            "v_mfma_scale_f32_16x16x128_f8f6f4 %[b1], v[248:255], %[p1], 0, %[one], %[one] op_sel_hi:[0,0,0]\n\t"
+            "v_mfma_scale_f32_16x16x128_f8f6f4 %[b0], %[sel], %[p0], 0, %[one], %[one] op_sel_hi:[0,0,0]\n\t"
+            "v_mfma_scale_f32_16x16x128_f8f6f4 %[b1], %[sel], %[p1], 0, %[one], %[one] op_sel_hi:[0,0,0]\n\t"
             // S^T(i+1) = K Q^T: sub-tile u, 64-wide chunk c, chunk-outer; each operand read two MFMAs ahead
             "ds_read_b128 v[248:251], %[kb] offset:4608\n\t"
             "ds_read_b128 v[252:255], %[kb] offset:4624\n\t"
@@ -593,7 +586,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
               [o0] "+v"(oacc[0]), [o1] "+v"(oacc[1]), [o2] "+v"(oacc[2]), [o3] "+v"(oacc[3]),
               [b0] "=&v"(b0), [b1] "=&v"(b1), "=&{v[240:247]}"(g0), "=&{v[248:255]}"(g1), [m0s] "=&s"(m0s)
             : [kb] "v"(kb), [vb] "v"(vb), [q0] "v"(qop[0]), [q1] "v"(qop[1]), [p0] "v"(pb[0]), [p1] "v"(pb[1]),
-              [selw] "v"(selw), [one] "v"(one), [c0] "v"(sc0), [c1] "v"(sc1), [mb] "s"(mb), [gs] "s"(gs),
+              [sel] "v"(selv), [one] "v"(one), [c0] "v"(sc0), [c1] "v"(sc1), [mb] "s"(mb), [gs] "s"(gs),
               [a0] "v"(st_goff[0]), [a1] "v"(st_goff[1]), [a2] "v"(st_goff[2]), [a3] "v"(st_goff[3]),
               [a4] "v"(st_goff[4]), [nr] "s"(nrounds), [cp] "s"(cp), [vt] "n"(VT ? 1 : 0)
             : "memory", "scc");
@@ -603,20 +596,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
             "s_nop 4\n\t"
             "s_mov_b32 %[m0s], m0\n\t"
             "s_waitcnt lgkmcnt(0)\n\t"
-            // row sums of P(i): the 0/1 selector in group 1, the first K operand read in group 0
-            "v_mov_b32 v248, %[selw]\n\t"
-            "v_mov_b32 v249, %[selw]\n\t"
-            "v_mov_b32 v250, %[selw]\n\t"
-            "v_mov_b32 v251, %[selw]\n\t"
-            "v_mov_b32 v252, %[selw]\n\t"
-            "v_mov_b32 v253, %[selw]\n\t"
-            "v_mov_b32 v254, %[selw]\n\t"
-            "v_mov_b32 v255, %[selw]\n\t"
+            // row sums of P(i) against the 0/1 selector; the first K operand read in group 0
             "ds_read_b128 v[240:243], %[kb]\n\t"
             "ds_read_b128 v[244:247], %[kb] offset:16\n\t"
-            "s_nop 1\n\t"
-            "v_mfma_scale_f32_16x16x128_f8f6f4 %[b0], v[248:255], %[p0], 0, %[one], %[one] op_sel_hi:[0,0,0]\n\t"
-            "v_mfma_scale_f32_16x16x128_f8f6f4 %[b1], v[248:255], %[p1], 0, %[one], %[one] op_sel_hi:[0,0,0]\n\t"
+            "v_mfma_scale_f32_16x16x128_f8f6f4 %[b0], %[sel], %[p0], 0, %[one], %[one] op_sel_hi:[0,0,0]\n\t"
+            "v_mfma_scale_f32_16x16x128_f8f6f4 %[b1], %[sel], %[p1], 0, %[one], %[one] op_sel_hi:[0,0,0]\n\t"
             // S^T(i+1) = K Q^T: sub-tile u, 64-wide chunk c, chunk-outer; each operand read two MFMAs ahead
             "ds_read_b128 v[248:251], %[kb] offset:6656\n\t"
             "ds_read_b128 v[252:255], %[kb] offset:6672\n\t"
@@ -870,7 +854,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
               [o0] "+v"(oacc[0]), [o1] "+v"(oacc[1]), [o2] "+v"(oacc[2]), [o3] "+v"(oacc[3]),
               [b0] "=&v"(b0), [b1] "=&v"(b1), "=&{v[240:247]}"(g0), "=&{v[248:255]}"(g1), [m0s] "=&s"(m0s)
             : [kb] "v"(kb), [vb] "v"(vb), [q0] "v"(qop[0]), [q1] "v"(qop[1]), [q2] "v"(qop[KC - 1]),
-              [p0] "v"(pb[0]), [p1] "v"(pb[1]), [selw] "v"(selw), [one] "v"(one), [c0] "v"(sc0), [c1] "v"(sc1),
+              [p0] "v"(pb[0]), [p1] "v"(pb[1]), [sel] "v"(selv), [one] "v"(one), [c0] "v"(sc0), [c1] "v"(sc1),
               [mb] "s"(mb), [gs] "s"(gs), [a0] "v"(st_goff[0]), [a1] "v"(st_goff[1]), [a2] "v"(st_goff[2]),
               [a3] "v"(st_goff[3]), [a4] "v"(st_goff[4]), [a5] "v"(st_goff[NR > 5 ? 5 : 4]),
               [a6] "v"(st_goff[NR > 6 ? 6 : 4]), [nr] "s"(nrounds), [cp] "s"(cp), [vt] "n"(VT ? 1 : 0)
