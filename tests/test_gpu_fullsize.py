@@ -73,6 +73,16 @@ def test_c2_fp8_b1_h32_s32768():
     assert r["lse_emu"] <= LSE_EMU_NATS and r["lse_fp64"] <= LSE_FP64_NATS
 
 
+@pytest.mark.parametrize("S", [4096, 8192, 16384])
+def test_c3_fp8_b1_h32_sweep(S):
+    """The FP8 lines of the S sweep that bench.py times (B1 H32 d128, lean P) at their full sizes."""
+    _case(f"C3 FP8 B1 H32 S{S} d128 lean P")
+    r = _fp8_full(synth.gaussian, 1, 32, S, 128, False, 10 + S // 4096, 12)
+    assert r["emu_maxabs"] <= TOL_EMU_MAXABS and r["emu_rms"] <= TOL_EMU_RMS
+    assert r["fp64_rms"] <= TOL_FP64_RMS_FP8
+    assert r["lse_emu"] <= LSE_EMU_NATS and r["lse_fp64"] <= LSE_FP64_NATS
+
+
 def test_c4_mla_b1_h16_s32768():
     _case("C4 MLA FP8 B1 H16 S32768 192/128 exact P")
     r = _fp8_full(synth.gaussian, 1, 16, 32768, 192, True, 1, 12)
